@@ -1,0 +1,186 @@
+"""Seeded synthetic workloads for PISA prefill and decode.
+
+This module only draws inputs: it holds no part of the method's arithmetic
+(no pooling, scoring, selection or attention).  The GPU path and the CPU
+oracle both consume the arrays it returns, so the two always see identical
+bytes.
+
+Shapes and value distributions follow the five workloads the path is
+measured on (tiny fp32 prefill, 4K / 32K / 256K bf16 prefill, and a
+64-sequence decode over a 131072-token context).  The pages that describe
+PISA measure selection on real model activations, which are not available
+here; these planted Gaussian inputs stand in for them.
+
+Recipe (every draw is ``numpy.random.default_rng([seed, tensor_id, ...])``):
+
+* ``u``  = unit vector, ``rng([seed, 99]).standard_normal(d)`` normalised.
+* ``Q[b, :, h, :]``   = ``rng([seed, 0, b, h]).standard_normal((N, d))`` + alpha_q * u
+* ``K[b, :, kvh, :]`` = ``rng([seed, 1, b, kvh]).standard_normal((N, d))``, plus
+  alpha_k * u on every key of ``n_plant`` leaf blocks chosen by
+  ``rng([seed, 98, b, kvh]).choice(M1, n_plant, replace=False)``.
+* ``V[b, :, kvh, :]`` = ``rng([seed, 2, b, kvh]).standard_normal((N, d))``
+* decode tokens: ``rng([seed, 10|11|12, b, head]).standard_normal((steps, d))``
+  for q / k_new / v_new.
+
+All draws are float32; shifts are added in float32, then the bf16
+workloads round to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+LEAF = 64      # C: raw keys per leaf block
+FANOUT = 2     # g: children per pyramid node above the leaves
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    seq_len: int          # prefill length N, or the prebuilt context length for decode
+    head_dim: int
+    n_q_heads: int
+    n_kv_heads: int
+    top_k: int
+    dtype: str            # "f32" or "bf16"
+    plant_blocks: int     # leaf blocks per (b, kvh) whose keys get alpha_k * u (0: none)
+    alpha_k: float
+    alpha_q: float
+    decode_steps: int = 0
+    block: int = LEAF
+    fanout: int = FANOUT
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_leaves(self) -> int:
+        return -(-self.seq_len // self.block)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _plant_count(frac: float, n_leaves: int) -> int:
+    return max(1, int(round(frac * n_leaves)))
+
+
+# The five workloads: tiny fp32 prefill, three bf16 prefills and the decode run.
+WORKLOADS = {
+    "tiny_f32_n1024": Workload("tiny_f32_n1024", seed=0, batch=1, seq_len=1024, head_dim=64,
+                               n_q_heads=4, n_kv_heads=1, top_k=4, dtype="f32",
+                               plant_blocks=2, alpha_k=3.0, alpha_q=1.5),
+    "prefill_n4096": Workload("prefill_n4096", seed=1, batch=1, seq_len=4096, head_dim=128,
+                              n_q_heads=16, n_kv_heads=1, top_k=16, dtype="bf16",
+                              plant_blocks=_plant_count(0.02, 64), alpha_k=2.0, alpha_q=1.0),
+    "prefill_n32768": Workload("prefill_n32768", seed=2, batch=2, seq_len=32768, head_dim=128,
+                               n_q_heads=32, n_kv_heads=2, top_k=32, dtype="bf16",
+                               plant_blocks=_plant_count(0.02, 512), alpha_k=2.0, alpha_q=1.0),
+    "prefill_n262144": Workload("prefill_n262144", seed=3, batch=1, seq_len=262144, head_dim=128,
+                                n_q_heads=16, n_kv_heads=1, top_k=16, dtype="bf16",
+                                plant_blocks=_plant_count(0.005, 4096), alpha_k=2.5, alpha_q=1.0),
+    "decode_b64_ctx131072": Workload("decode_b64_ctx131072", seed=4, batch=64, seq_len=131072,
+                                     head_dim=128, n_q_heads=32, n_kv_heads=8, top_k=16,
+                                     dtype="bf16", plant_blocks=0, alpha_k=0.0, alpha_q=0.0,
+                                     decode_steps=256),
+}
+
+
+# ----------------------------------------------------------------------------- bf16 helpers
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    rounded = b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def quantise(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the workload's storage type, returned as float32."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return bf16_bits_to_f32(round_bf16_bits(x))
+
+
+# ----------------------------------------------------------------------------- draws
+def _rng(*ids: int) -> np.random.Generator:
+    return np.random.default_rng([int(i) for i in ids])
+
+
+def planted_direction(w: Workload) -> np.ndarray:
+    u = _rng(w.seed, 99).standard_normal(w.head_dim)
+    return (u / np.linalg.norm(u)).astype(np.float32)
+
+
+def planted_blocks(w: Workload, b: int, kvh: int, n_leaves: int | None = None) -> np.ndarray:
+    m1 = w.n_leaves if n_leaves is None else n_leaves
+    if w.plant_blocks <= 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(_rng(w.seed, 98, b, kvh).choice(m1, min(w.plant_blocks, m1), replace=False))
+
+
+def q_slice(w: Workload, b: int, h: int, n: int | None = None) -> np.ndarray:
+    """Q[b, :n, h, :] as float32 values already rounded to the workload dtype."""
+    n = w.seq_len if n is None else n
+    x = _rng(w.seed, 0, b, h).standard_normal((n, w.head_dim), dtype=np.float32)
+    if w.alpha_q:
+        x += np.float32(w.alpha_q) * planted_direction(w)
+    return quantise(x, w.dtype)
+
+
+def k_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
+    n = w.seq_len if n is None else n
+    x = _rng(w.seed, 1, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
+    if w.plant_blocks:
+        shift = np.float32(w.alpha_k) * planted_direction(w)
+        for j in planted_blocks(w, b, kvh, -(-n // w.block)):
+            x[j * w.block:(j + 1) * w.block] += shift
+    return quantise(x, w.dtype)
+
+
+def v_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
+    n = w.seq_len if n is None else n
+    x = _rng(w.seed, 2, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
+    return quantise(x, w.dtype)
+
+
+def decode_tokens(w: Workload, which: str, b: int, h: int) -> np.ndarray:
+    """New per-step vectors [steps, d] for 'q', 'k' or 'v' of sequence b, head h."""
+    tid = {"q": 10, "k": 11, "v": 12}[which]
+    x = _rng(w.seed, tid, b, h).standard_normal((w.decode_steps, w.head_dim), dtype=np.float32)
+    return quantise(x, w.dtype)
+
+
+def prefill_inputs(w: Workload, batches=None, n: int | None = None):
+    """Full Q [B, n, Hq, d], K and V [B, n, Hkv, d] as float32 arrays (values in the workload dtype).
+
+    ``batches`` restricts generation to a subset of sequence indices (the
+    arrays then hold those sequences in order); ``n`` truncates the length.
+    """
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    n = w.seq_len if n is None else n
+    q = np.empty((len(batches), n, w.n_q_heads, w.head_dim), dtype=np.float32)
+    k = np.empty((len(batches), n, w.n_kv_heads, w.head_dim), dtype=np.float32)
+    v = np.empty_like(k)
+    for bi, b in enumerate(batches):
+        for h in range(w.n_q_heads):
+            q[bi, :, h] = q_slice(w, b, h, n)
+        for h in range(w.n_kv_heads):
+            k[bi, :, h] = k_slice(w, b, h, n)
+            v[bi, :, h] = v_slice(w, b, h, n)
+    return q, k, v
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array for the device: float32 as is, bf16 as uint16 bit patterns."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return round_bf16_bits(x)

@@ -1,0 +1,33 @@
+"""CPU oracle for PISA hierarchical block selection and block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, float64 NumPy
+statement of what the GPU path computes.  Only the test suite, the smoke
+check and the benchmark's CPU-baseline leg may import it; the library and
+its Python binding never do, and nothing here imports them.
+
+Source of every rule: the paper-summary page "Block Sparse Attention with
+Log-Linear Complexity" (Tang, Qin, Pan, Li, Liu), sections Prerequisites,
+Core method and Method steps.  Each function names the passage it follows.
+
+Modules
+-------
+``pisa``           level-by-level vectorised oracle (pyramid, routing, leaf
+                   LSE, top-K, attention, decode).
+``per_query``      an independently written per-query routine (pure-Python
+                   loops, its own pyramid, its own LSE) used to pin ``pisa``
+                   on tiny inputs; also a brute-force flat top-K.
+
+Parity status
+-------------
+Pinned: pyramid (closed form over full spans, hand-derived partial-node
+fixture), LSE (high-precision Decimal brute force, bounds, Taylor
+expansion), flat equivalence when every level keeps all candidates (brute
+force), K >= number of leaves (textbook dense causal attention), attention
+weights summing to one, selection-set invariants (size formula, causal
+validity, lower-index tie rule), decode (incremental update == rebuild,
+decode step == prefill of the last token).
+The general hierarchical case (K smaller than half the leaves) has no worked
+example on the pages: it is pinned only by agreement of the two
+independently written routines plus the invariants above ("parity
+unpinned" beyond that).
+"""

@@ -1,0 +1,276 @@
+"""Pins for the CPU oracle: closed forms, brute force, hand-derived fixtures and invariants.
+
+Everything here runs on the CPU in seconds.  Each test states which rule of
+the paper-summary page "Block Sparse Attention with Log-Linear Complexity"
+it pins, and checks the oracle against something other than itself.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import per_query
+from oracle import pisa
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------- pyramid
+def test_pyramid_full_spans_equal_span_means():
+    """Method steps, first step: with n = C * g**(L-1) every node is the mean of its key span."""
+    C, g = 4, 2
+    k = _rand(1, 64, 3)
+    pyr = pisa.build_pyramid(k, C, g)
+    assert [lv.shape[0] for lv in pyr] == [16, 8, 4, 2, 1]
+    for lvl, nodes in enumerate(pyr, start=1):
+        span = C * g ** (lvl - 1)
+        for i in range(nodes.shape[0]):
+            np.testing.assert_allclose(nodes[i], k[i * span:(i + 1) * span].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_pyramid_partial_nodes_golden():
+    """Partial nodes are the unweighted mean of existing children (hand-derived fixture)."""
+    with open(os.path.join(GOLDEN, "pyramid_partial.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        pyr = pisa.build_pyramid(np.array(case["keys"], dtype=float), C=2, g=2)
+        assert len(pyr) == len(case["levels"])
+        for got, want in zip(pyr, case["levels"]):
+            np.testing.assert_array_equal(got, np.array(want, dtype=float))
+
+
+def test_pyramid_invariant_to_key_order_within_span():
+    C, g = 8, 2
+    k = _rand(2, 64, 4)
+    perm = k.copy()
+    perm[8:16] = perm[8:16][::-1]
+    a, b = pisa.build_pyramid(k, C, g), pisa.build_pyramid(perm, C, g)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-14)
+
+
+@pytest.mark.parametrize("C", [1, 2, 4])
+def test_incremental_update_equals_rebuild(C):
+    """Method steps, third step: updating the new leaf and its ancestors equals a rebuild."""
+    k = _rand(3, 70, 3)
+    pyr = pisa.build_pyramid(k[:1], C, 2)
+    for n in range(2, 71):
+        pyr = pisa.update_pyramid(pyr, k, n, C, 2)
+        ref = pisa.build_pyramid(k[:n], C, 2)
+        assert len(pyr) == len(ref), n
+        for x, y in zip(pyr, ref):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_level_sizes():
+    assert pisa.level_sizes(1024, 64, 2) == [16, 8, 4, 2, 1]
+    assert pisa.level_sizes(262144, 64, 2)[0] == 4096 and len(pisa.level_sizes(262144)) == 13
+    assert pisa.level_sizes(131073, 64, 2)[:2] == [2049, 1025] and len(pisa.level_sizes(131073)) == 13
+    assert len(pisa.level_sizes(131072)) == 12
+
+
+# ----------------------------------------------------------------------------- LSE
+def test_logsumexp_matches_50_digit_decimal():
+    """Prerequisites, LogSumExp: log sum exp z, checked against 50-digit arithmetic."""
+    rng = np.random.default_rng(4)
+    for scale in (1e-3, 1.0, 30.0, 300.0):
+        z = rng.standard_normal(64) * scale
+        assert abs(pisa.logsumexp(z) - per_query.lse_exact(list(z))) <= 1e-13 * max(1.0, abs(per_query.lse_exact(list(z))))
+
+
+def test_logsumexp_bounds_and_identical_entries():
+    """Prerequisites, LogSumExp: smooth upper bound of max; m equal entries give z + log m."""
+    rng = np.random.default_rng(5)
+    for m in (1, 2, 7, 64):
+        z = rng.standard_normal(m) * 3
+        s = pisa.logsumexp(z)
+        assert z.max() <= s <= z.max() + math.log(m) + 1e-12
+        assert abs(pisa.logsumexp(np.full(m, 0.37)) - (0.37 + math.log(m))) < 1e-14
+
+
+def test_logsumexp_taylor_expansion():
+    """Core method: LSE = log m + mean + Var/2 + O(eps^3) for logits of size eps."""
+    x = np.random.default_rng(6).standard_normal(64)
+    res = []
+    for eps in (1e-1, 5e-2, 2.5e-2):
+        z = eps * x
+        res.append(abs(pisa.logsumexp(z) - (math.log(64) + z.mean() + 0.5 * z.var())))
+    assert 5.0 < res[0] / res[1] < 11.0 and 5.0 < res[1] / res[2] < 11.0   # cubic: ratio ~8
+
+
+def test_leaf_lse_exact_and_causal():
+    """Core method eq. 21 at the leaf level: exact LSE over the block's raw keys at positions <= t."""
+    q = _rand(7, 3, 8)
+    k = _rand(8, 40, 8)
+    scale = 1 / math.sqrt(8)
+    for j, t in [(0, 39), (1, 25), (2, 33), (1, 16)]:
+        got = pisa.leaf_lse(q, k, j, t, C=16)
+        keys = [k[r] for r in range(j * 16, min((j + 1) * 16, 40)) if r <= t]
+        want = [per_query.lse_exact([float(np.dot(qh, kk)) * scale for kk in keys]) for qh in q]
+        np.testing.assert_allclose(got, want, rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- routing
+def test_route_golden_hand_examples():
+    """Hand-derived routing examples with a deliberate difference from flat top-1 and an exact tie."""
+    with open(os.path.join(GOLDEN, "route_tiny.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        k = np.array(case["keys"], dtype=float)[:, None]
+        pyr = pisa.build_pyramid(k, C=1, g=2)
+        sel, _ = pisa.route(np.ones((1, 1, 1)), k, pyr, np.array([case["t"]]), K=1, C=1, g=2, scale=1.0)
+        assert list(sel[0]) == case["expected"], case
+        heads = [[1.0]]
+        assert per_query.select([[x] for x in case["keys"]], heads, case["t"], 1, C=1, g=2, scale=1.0) == case["expected"]
+
+
+@pytest.mark.parametrize("C,G,n", [(4, 1, 40), (4, 2, 64), (8, 4, 72), (2, 3, 33)])
+def test_flat_equivalence_when_every_level_is_kept(C, G, n):
+    """Core method: when K >= ceil(M1/2), no level above the leaves is cut, so the result is the
+    brute-force flat top-K over exact leaf LSE (summed over heads) of all valid leaves."""
+    rng = np.random.default_rng(10 + C + G + n)
+    k = rng.standard_normal((n, 6))
+    q = rng.standard_normal((n, G, 6)) + 0.5
+    m1 = -(-n // C)
+    K = -(-m1 // 2)
+    pyr = pisa.build_pyramid(k, C, 2)
+    sel, _ = pisa.route(q, k, pyr, np.arange(n), K, C, 2)
+    for t in range(n):
+        want = per_query.flat_select(k.tolist(), q[t].tolist(), t, K, C)
+        assert [int(x) for x in sel[t] if x >= 0] == want, t
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_agrees_with_independent_per_query_routine(seed):
+    """General hierarchical case (K < ceil(M1/2)): two independently written routines agree."""
+    rng = np.random.default_rng(100 + seed)
+    C = [2, 4, 4, 8, 2, 4][seed]
+    G = [1, 2, 4, 2, 3, 1][seed]
+    K = [2, 2, 3, 2, 3, 4][seed]
+    n = [50, 96, 128, 130, 77, 200][seed]
+    k = rng.standard_normal((n, 5))
+    k[C * 3:C * 4] += 1.5                         # one planted block
+    q = rng.standard_normal((n, G, 5)) + 0.3
+    pyr = pisa.build_pyramid(k, C, 2)
+    sel, gap = pisa.route(q, k, pyr, np.arange(n), K, C, 2)
+    ref_pyr = per_query.Pyramid(k.tolist(), C, 2)
+    for t in range(n):
+        want = per_query.select(k.tolist(), q[t].tolist(), t, K, C, 2, pyr=ref_pyr)
+        assert [int(x) for x in sel[t] if x >= 0] == want, (t, gap[t])
+
+
+def test_selection_size_validity_and_candidate_bound():
+    """|I_t| = min(K, floor(t/C)+1), distinct, ascending, causally valid; at most gK candidates per level."""
+    rng = np.random.default_rng(11)
+    C, g, K, n = 4, 2, 3, 150
+    k = rng.standard_normal((n, 4))
+    q = rng.standard_normal((n, 2, 4))
+    pyr = pisa.build_pyramid(k, C, g)
+    sel, gap, rec = pisa.route(q, k, pyr, np.arange(n), K, C, g, record=True)
+    for t in range(n):
+        s = [int(x) for x in sel[t] if x >= 0]
+        assert len(s) == min(K, t // C + 1)
+        assert s == sorted(set(s)) and all(j * C <= t for j in s)
+        assert all(x == -1 for x in sel[t][len(s):])
+    for counts in rec["counts"]:
+        assert counts.max() <= g * K
+
+
+def test_ties_go_to_the_lower_index():
+    """Identical keys tie at every level: the K lowest leaves win (tie rule reading)."""
+    C, g, K = 4, 2, 3
+    n = C * 16
+    k = np.tile(_rand(12, 1, 5), (n, 1))
+    q = _rand(13, 1, 2, 5)
+    pyr = pisa.build_pyramid(k, C, g)
+    sel, gap = pisa.route(q, k, pyr, np.array([n - 1]), K, C, g)
+    assert list(sel[0]) == [0, 1, 2] and gap[0] == 0.0
+    # two identical blocks compete for one slot: the lower one wins
+    k2 = _rand(14, 8, 5)
+    k2[4:8] = k2[0:4]
+    pyr2 = pisa.build_pyramid(k2, C, g)
+    sel2, _ = pisa.route(_rand(15, 1, 1, 5), k2, pyr2, np.array([7]), 1, C, g)
+    assert list(sel2[0]) == [0]
+
+
+def test_head_sum_is_group_invariant_and_single_head_reduces():
+    """Method steps eq. 22: u sums the group's head scores (order of heads does not matter)."""
+    rng = np.random.default_rng(16)
+    C, K, n = 4, 2, 96
+    k = rng.standard_normal((n, 6))
+    q = rng.standard_normal((n, 4, 6))
+    pyr = pisa.build_pyramid(k, C, 2)
+    a, _ = pisa.route(q, k, pyr, np.arange(n), K, C, 2)
+    b, _ = pisa.route(q[:, ::-1], k, pyr, np.arange(n), K, C, 2)
+    np.testing.assert_array_equal(a, b)
+    one, _ = pisa.route(q[:, :1], k, pyr, np.arange(n), K, C, 2)
+    for t in range(0, n, 7):
+        assert [int(x) for x in one[t] if x >= 0] == per_query.select(k.tolist(), q[t, :1].tolist(), t, K, C, 2)
+
+
+# ----------------------------------------------------------------------------- attention
+def test_all_leaves_selected_gives_dense_causal_attention():
+    """K >= M1: every valid leaf is kept and attention is textbook dense causal attention."""
+    rng = np.random.default_rng(17)
+    C, n, G = 8, 60, 2
+    k, v = rng.standard_normal((n, 5)), rng.standard_normal((n, 5))
+    q = rng.standard_normal((n, G, 5))
+    out = pisa.prefill(q, k, v, K=8, C=C)
+    for t in range(n):
+        assert [int(x) for x in out["sel"][t] if x >= 0] == list(range(t // C + 1))
+    np.testing.assert_allclose(out["o"], pisa.dense_causal_attention(q, k, v, np.arange(n)), atol=1e-12)
+
+
+def test_attention_weights_sum_to_one_and_first_token():
+    rng = np.random.default_rng(18)
+    C, n = 4, 40
+    k, v = rng.standard_normal((n, 3)), rng.standard_normal((n, 3))
+    q = rng.standard_normal((n, 2, 3)) * 4
+    pyr = pisa.build_pyramid(k, C)
+    ts = np.arange(n)
+    sel, _ = pisa.route(q, k, pyr, ts, 2, C)
+    o, lse, wsum = pisa.attention(q, k, v, sel, ts, C)
+    np.testing.assert_allclose(wsum, 1.0, atol=1e-13)
+    np.testing.assert_allclose(o[0], np.tile(v[0], (2, 1)), atol=1e-15)
+
+
+def test_attention_matches_per_query_routine():
+    rng = np.random.default_rng(19)
+    C, n = 4, 30
+    k, v = rng.standard_normal((n, 3)), rng.standard_normal((n, 3))
+    q = rng.standard_normal((n, 2, 3))
+    sel = np.array([[0, 2, -1], [1, 3, 5]])
+    ts = np.array([9, 23])
+    o, _, _ = pisa.attention(q[ts], k, v, sel, ts, C)
+    for r, t in enumerate(ts):
+        want = per_query.attend(k.tolist(), v.tolist(), q[t].tolist(), [x for x in sel[r] if x >= 0], t, C)
+        np.testing.assert_allclose(o[r], want, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- decode
+def test_decode_step_equals_prefill_of_last_token():
+    """Method steps, third step: decode at length n+1 equals prefill's result for token n."""
+    rng = np.random.default_rng(20)
+    C, K, G, d = 4, 2, 2, 5
+    n0, steps = 29, 40                 # crosses 32 and 64 keys: new leaves and a new root level
+    k = rng.standard_normal((n0 + steps, d))
+    v = rng.standard_normal((n0 + steps, d))
+    q = rng.standard_normal((n0 + steps, G, d))
+    st = pisa.DecodeState(k[:n0], v[:n0], C)
+    for s in range(steps):
+        n = n0 + s
+        sel, gap, o, lse = st.step(q[n], k[n], v[n], K)
+        ref_pyr = pisa.build_pyramid(k[:n + 1], C)
+        assert len(st.pyr) == len(ref_pyr)
+        for x, y in zip(st.pyr, ref_pyr):
+            np.testing.assert_array_equal(x, y)
+        want_sel, _ = pisa.route(q[n:n + 1], k[:n + 1], ref_pyr, np.array([n]), K, C)
+        np.testing.assert_array_equal(sel, want_sel[0])
+        want_o, _, _ = pisa.attention(q[n:n + 1], k[:n + 1], v[:n + 1], want_sel, np.array([n]), C)
+        np.testing.assert_allclose(o, want_o[0], atol=1e-13)
