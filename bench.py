@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Prefill throughput of the PISA hot path on one MI355X.
+
+One step = build the key pyramid, select the top-K leaf blocks of every query
+token (routing, clustering, exact leaf LSE, top-K) and run block-sparse
+attention over them, for the whole batch of one workload, with inputs already
+resident in HBM.  Prints ONE JSON line (see the design notes for the fields).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload prefill_n262144]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from hierarchical_top_selection_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+# ----------------------------------------------------------------------------- CPU baseline (oracle)
+_CPU = {}
+
+
+def _cpu_init(q, k, v, pyr, K):
+    from threadpoolctl import threadpool_limits
+
+    threadpool_limits(1)
+    _CPU.update(q=q, k=k, v=v, pyr=pyr, K=K)
+
+
+def _cpu_chunk(ts):
+    from oracle import pisa as oracle
+
+    ts = np.asarray(ts)
+    sel, _ = oracle.route(_CPU["q"][ts], _CPU["k"], _CPU["pyr"], ts, _CPU["K"])
+    oracle.attention(_CPU["q"][ts], _CPU["k"], _CPU["v"], sel, ts)
+    return len(ts)
+
+
+def cpu_baseline(w: W.Workload, seconds: float) -> dict:
+    """The fp64 oracle on a time-bounded sample of (b=0, kvh=0) tokens, extrapolated to the workload."""
+    import multiprocessing as mp
+
+    from oracle import pisa as oracle
+
+    G = w.group
+    q = np.stack([W.draw(w, "q", 0, h) for h in range(G)], axis=1).astype(np.float64)
+    k = W.draw(w, "k", 0, 0).astype(np.float64)
+    v = W.draw(w, "v", 0, 0).astype(np.float64)
+    t0 = time.perf_counter()
+    pyr = oracle.build_pyramid(k)
+    t_pyr = time.perf_counter() - t0
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    order = np.random.default_rng(12345).permutation(w.seq_len)
+    chunks = [np.sort(order[i:i + 16]) for i in range(0, w.seq_len, 16)]
+    done = 0
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_cpu_init, initargs=(q, k, v, pyr, w.top_k)) as pool:
+        t0 = time.perf_counter()
+        for n in pool.imap_unordered(_cpu_chunk, chunks):
+            done += n
+            if time.perf_counter() - t0 > seconds:
+                break
+        elapsed = time.perf_counter() - t0
+        pool.terminate()
+    units = w.batch * w.n_kv_heads
+    full_s = units * t_pyr + units * w.seq_len * elapsed / done
+    return {"value": w.batch * w.seq_len / full_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} query tokens of (b=0, kvh=0) drawn uniformly from the {w.seq_len}-token sequence "
+                      f"(fp64 NumPy routing, leaf LSE, top-K and attention) in {elapsed:.1f} s on {workers} "
+                      f"processes, plus one pyramid build ({t_pyr:.2f} s); extrapolated to "
+                      f"{units} x {w.seq_len} tokens"}
+
+
+# ----------------------------------------------------------------------------- GPU
+def _device_inputs(w: W.Workload):
+    import torch
+
+    q, k, v = W.prefill_inputs(w, bits=True)
+
+    def dev(x):
+        if w.dtype == "f32":
+            return torch.from_numpy(x).to("cuda:0")
+        return torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+    return dev(q), dev(k), dev(v)
+
+
+def attention_flops(sel, n: int, group: int, d: int) -> float:
+    """4 d flops per (query head, valid key): keys of the selected blocks at positions <= t."""
+    import torch
+
+    t = torch.arange(n, device=sel.device, dtype=torch.int64).view(1, 1, n, 1)
+    j = sel.to(torch.int64)
+    valid = torch.clamp(torch.minimum(t - 64 * j + 1, torch.full_like(j, 64)), min=0)
+    valid = torch.minimum(valid, torch.clamp(n - 64 * j, min=0))
+    valid = torch.where(j >= 0, valid, torch.zeros_like(valid))
+    return float(valid.sum().item()) * group * 4.0 * d
+
+
+def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
+    import torch
+
+    from hierarchical_top_selection_amd import binding
+
+    q, k, v = _device_inputs(w)
+    B, N, Hq, d = q.shape
+    K = w.top_k
+    pyr = torch.empty((B, w.n_kv_heads, binding.pyramid_nodes(N), d), dtype=torch.float32, device=q.device)
+    cfg = binding.make_cfg(B, N, Hq, w.n_kv_heads, d, K, q.dtype)
+    ws = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    sel = torch.empty((B, w.n_kv_heads, N, K), dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.build_pyramid(k, out=pyr)
+        if ev is not None:
+            ev[1].record()
+        binding.select_blocks(q, k, pyr, K, workspace=ws, out=sel)
+        if ev is not None:
+            ev[2].record()
+        binding.sparse_attn_fwd(q, k, v, sel, out=o)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    pyr_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in events) / steps
+    flops = attention_flops(sel, N, w.group, d)
+    return {"workload": w, "ms_per_step": wall_ms, "pyramid_ms": pyr_ms, "select_ms": sel_ms,
+            "attn_ms": attn_ms, "tokens_per_s": B * N / (wall_ms / 1e3), "attn_flops": flops}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_n262144")
+    ap.add_argument("--also", default="prefill_n32768", help="comma-separated extra workloads to report")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; runs on more than one GPU are not supported "
+              "(the design notes describe how it would shard)", file=sys.stderr)
+        return 2
+    w = W.WORKLOADS[args.workload]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)   # before any GPU use
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    main_run = run_workload(w, args.steps, args.warmup)
+    extra = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        r = run_workload(W.WORKLOADS[name], args.steps, args.warmup)
+        extra[name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                       "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"]}
+    attn_tflops = main_run["attn_flops"] / (main_run["attn_ms"] * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    line = {
+        "metric": "prefill tokens/s (select+sparse attn)",
+        "value": main_run["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_run["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block, "fanout": w.fanout,
+                   "top_k": w.top_k, "parallelism": "single_gpu"},
+        "pyramid_ms": main_run["pyramid_ms"],
+        "select_ms": main_run["select_ms"],
+        "attn_ms": main_run["attn_ms"],
+        "roofline": {"kernel": "attention_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None},
+        "cpu_baseline": cpu,
+        "also": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

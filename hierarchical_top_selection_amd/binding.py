@@ -1,0 +1,213 @@
+"""Python binding of libpisa.so: the C ABI of include/pisa.h with torch tensors.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the shared library.  The library is loaded on first use; if it has not been
+built, or cannot be loaded, every call raises -- there is no fallback.
+
+Tensors (device, contiguous in the head_dim axis):
+  q  [B, N, Hq, d]   k, v  [B, N, Hkv, d]   bfloat16 or float32
+  pyramid            float32 [B, Hkv, pyramid_nodes(capacity), d]
+  selection          int32 [B, Hkv, N, K], ascending leaf ids, -1 padded
+Work is enqueued on torch's current stream of the tensors' device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpisa.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "pisa.h")
+
+LEAF = 64
+FANOUT = 2
+PISA_F32, PISA_BF16 = 0, 1
+
+
+class PisaCfg(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("fanout", ctypes.c_int32), ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class PisaTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+_P = ctypes.POINTER
+_SIGNATURES = {
+    "pisa_abi_version": (ctypes.c_int, []),
+    "pisa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pisa_last_hip_error": (ctypes.c_int, []),
+    "pisa_pyramid_nodes": (ctypes.c_int64, [ctypes.c_int32]),
+    "pisa_pyramid_bytes": (ctypes.c_size_t, [_P(PisaCfg), ctypes.c_int32]),
+    "pisa_build_pyramid": (ctypes.c_int, [_P(PisaCfg), PisaTensor, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
+    "pisa_select_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
+    "pisa_select_blocks": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
+                                            PisaTensor, ctypes.c_void_p, ctypes.c_void_p]),
+    "pisa_decode_step": (ctypes.c_int, [_P(PisaCfg), ctypes.c_int32, PisaTensor, PisaTensor, PisaTensor,
+                                        PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p, PisaTensor,
+                                        ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (raises if it is missing or incomplete)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m hierarchical_top_selection_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/pisa.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(pisa_\w+)\s*\(", text)))
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        msg = lib().pisa_status_string(status).decode()
+        raise RuntimeError(f"{name} failed: {msg} (status {status}, hip error {lib().pisa_last_hip_error()})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PISA_BF16
+    if t.dtype == torch.float32:
+        return PISA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: expected bfloat16 or float32")
+
+
+def _tensor(t: torch.Tensor, token_axis: bool = True) -> PisaTensor:
+    if t.stride(-1) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    if token_axis:
+        sb, st, sh = t.stride(0), t.stride(1), t.stride(2)
+    else:
+        sb, st, sh = t.stride(0), 0, t.stride(1)
+    return PisaTensor(t.data_ptr(), sb, st, sh)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_cfg(batch: int, seq_len: int, n_q_heads: int, n_kv_heads: int, head_dim: int, top_k: int,
+             dtype: torch.dtype, scale: float = 0.0) -> PisaCfg:
+    code = PISA_BF16 if dtype == torch.bfloat16 else PISA_F32
+    return PisaCfg(batch, seq_len, n_q_heads, n_kv_heads, head_dim, LEAF, FANOUT, top_k, code, scale)
+
+
+def pyramid_nodes(capacity: int) -> int:
+    return int(lib().pisa_pyramid_nodes(capacity))
+
+
+def _cfg_from(q_or_none, k: torch.Tensor, top_k: int, scale: float, seq_len: int | None = None) -> PisaCfg:
+    B, N, Hkv, d = k.shape
+    Hq = q_or_none.shape[2] if q_or_none is not None else Hkv
+    cfg = make_cfg(B, N if seq_len is None else seq_len, Hq, Hkv, d, top_k, k.dtype, scale)
+    _dtype_code(k)
+    return cfg
+
+
+def build_pyramid(k: torch.Tensor, n: int | None = None, capacity: int | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Mean-pooled key pyramid of k [B, >=n, Hkv, d] for length n, laid out for `capacity` keys."""
+    B, N, Hkv, d = k.shape
+    n = N if n is None else n
+    capacity = n if capacity is None else capacity
+    cfg = _cfg_from(None, k, 1, 0.0, seq_len=capacity)
+    nodes = pyramid_nodes(capacity)
+    if out is None:
+        out = torch.empty((B, Hkv, nodes, d), dtype=torch.float32, device=k.device)
+    elif out.shape != (B, Hkv, nodes, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("pyramid buffer has the wrong shape, dtype or layout")
+    _check("pisa_build_pyramid", lib().pisa_build_pyramid(ctypes.byref(cfg), _tensor(k), n, capacity,
+                                                         ctypes.c_void_p(out.data_ptr()), _stream(k)))
+    return out
+
+
+def select_workspace_bytes(cfg: PisaCfg) -> int:
+    return int(lib().pisa_select_workspace_bytes(ctypes.byref(cfg)))
+
+
+def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: int, scale: float = 0.0,
+                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  return_scores: bool = False):
+    """Hierarchical top-K leaf selection: int32 [B, Hkv, N, K] (and float32 scores if asked)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    cfg = _cfg_from(q, k, top_k, scale)
+    need = select_workspace_bytes(cfg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hkv, N, top_k), dtype=torch.int32, device=q.device)
+    scores = torch.empty((B, Hkv, N, top_k), dtype=torch.float32, device=q.device) if return_scores else None
+    _check("pisa_select_blocks", lib().pisa_select_blocks(
+        ctypes.byref(cfg), _tensor(q), _tensor(k), ctypes.c_void_p(pyr.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(scores.data_ptr() if scores is not None else 0),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return (out, scores) if return_scores else out
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, scale: float = 0.0,
+                    out: torch.Tensor | None = None, return_lse: bool = False):
+    """Attention over the selected blocks: o [B, N, Hq, d] (and row LSE [B, Hq, N] if asked)."""
+    B, N, Hq, d = q.shape
+    top_k = sel.shape[-1]
+    cfg = _cfg_from(q, k, top_k, scale)
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, k.shape[2], N, top_k):
+        raise ValueError("selection must be a contiguous int32 [B, Hkv, N, K] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _check("pisa_sparse_attn_fwd", lib().pisa_sparse_attn_fwd(
+        ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()),
+        _tensor(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, pyr: torch.Tensor, n_ctx: int, top_k: int, scale: float = 0.0,
+                out: torch.Tensor | None = None, sel_out: torch.Tensor | None = None):
+    """One decode step for every sequence: q [B, Hq, d], k_new/v_new [B, Hkv, d], caches [B, cap, Hkv, d].
+
+    Appends at position n_ctx, updates the pyramid in place and returns (o [B, Hq, d], sel [B, Hkv, K]).
+    """
+    B, cap, Hkv, d = k_cache.shape
+    Hq = q.shape[1]
+    cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, k_cache.dtype, scale)
+    _dtype_code(k_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if sel_out is None:
+        sel_out = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
+    _check("pisa_decode_step", lib().pisa_decode_step(
+        ctypes.byref(cfg), n_ctx, _tensor(q, False), _tensor(k_new, False), _tensor(v_new, False),
+        _tensor(k_cache), _tensor(v_cache), ctypes.c_void_p(pyr.data_ptr()), ctypes.c_void_p(sel_out.data_ptr()),
+        _tensor(out, False), _stream(q)))
+    return out, sel_out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

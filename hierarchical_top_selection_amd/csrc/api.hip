@@ -1,0 +1,251 @@
+// api.hip - the C ABI declared in include/pisa.h: host-side validation, pyramid
+// geometry, workspace carving and kernel launch order.  Nothing here allocates
+// or synchronises; every call enqueues on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "pisa.h"
+
+namespace {
+
+using pisa::Levels;
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxSeqSelect = 1000000;     // leaf counters of one window must fit in LDS
+constexpr int kMaxSeq = (1 << 25) - 1;     // packed (token << 6 | slot) fits int32
+constexpr int kWindow = 1024;              // tokens per Stage-2 clustering window
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+// Level sizes for length n laid out for `capacity` keys (capacity >= n >= 1).
+Levels make_levels(int n, int capacity) {
+  Levels lv;
+  memset(&lv, 0, sizeof(lv));
+  int m = (capacity + pisa::kLeaf - 1) / pisa::kLeaf;
+  int64_t off = 0;
+  int level = 0;
+  while (true) {
+    lv.offset[level] = off;
+    off += m;
+    ++level;
+    if (m == 1) break;
+    m = (m + 1) / 2;
+  }
+  lv.nodes = off;
+  int cur = (n + pisa::kLeaf - 1) / pisa::kLeaf;
+  int count = 0;
+  while (true) {
+    lv.size[count++] = cur;
+    if (cur == 1) break;
+    cur = (cur + 1) / 2;
+  }
+  lv.count = count;
+  return lv;
+}
+
+pisa_status check_cfg(const pisa_cfg* c) {
+  if (!c) return PISA_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->seq_len < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->top_k < 1)
+    return PISA_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads != 0) return PISA_ERR_INVALID_ARG;
+  if (c->dtype != PISA_F32 && c->dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (c->block != pisa::kLeaf || c->fanout != pisa::kFanout) return PISA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PISA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PISA_ERR_UNSUPPORTED;
+  if (c->top_k > 32) return PISA_ERR_UNSUPPORTED;
+  if (c->seq_len > kMaxSeq) return PISA_ERR_UNSUPPORTED;
+  return PISA_OK;
+}
+
+pisa_status check_tensor(const void* ptr, int64_t sb, int64_t st, int64_t sh) {
+  if (!aligned16(ptr)) return PISA_ERR_INVALID_ARG;
+  if (sb < 0 || st < 0 || sh < 0 || (sb % 8) || (st % 8) || (sh % 8)) return PISA_ERR_INVALID_ARG;
+  return PISA_OK;
+}
+
+float resolve_scale(const pisa_cfg* c) {
+  return c->scale > 0.f ? c->scale : 1.0f / sqrtf((float)c->head_dim);
+}
+
+pisa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PISA_OK;
+  g_last_hip_error = (int)e;
+  return PISA_ERR_HIP;
+}
+
+struct SelectWorkspace {
+  size_t cand, leaf_u, pairs, leaf_off, total;
+  int n_windows;
+};
+
+SelectWorkspace select_layout(const pisa_cfg* c) {
+  SelectWorkspace w;
+  const int64_t bh = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t slots = bh * c->seq_len * 2 * c->top_k;
+  const int m1 = (c->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
+  w.n_windows = (c->seq_len + kWindow - 1) / kWindow;
+  w.cand = 0;
+  w.leaf_u = align256(w.cand + slots * 4);
+  w.pairs = align256(w.leaf_u + slots * 4);
+  w.leaf_off = align256(w.pairs + slots * 4);
+  w.total = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pisa_abi_version(void) { return PISA_ABI_VERSION; }
+
+const char* pisa_status_string(pisa_status s) {
+  switch (s) {
+    case PISA_OK: return "ok";
+    case PISA_ERR_INVALID_ARG: return "invalid argument";
+    case PISA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PISA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PISA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int pisa_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t pisa_pyramid_nodes(int32_t capacity) {
+  if (capacity < 1) return 0;
+  return make_levels(1, capacity).nodes;
+}
+
+size_t pisa_pyramid_bytes(const pisa_cfg* cfg, int32_t capacity) {
+  if (check_cfg(cfg) != PISA_OK || capacity < 1) return 0;
+  return (size_t)cfg->batch * cfg->n_kv_heads * pisa_pyramid_nodes(capacity) * cfg->head_dim * sizeof(float);
+}
+
+pisa_status pisa_build_pyramid(const pisa_cfg* cfg, pisa_tensor k, int32_t n, int32_t capacity, float* pyr,
+                               void* stream) {
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  if (n < 1 || capacity < n || capacity > kMaxSeq) return PISA_ERR_INVALID_ARG;
+  if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
+  if (!aligned16(pyr)) return PISA_ERR_INVALID_ARG;
+  pisa::PyramidArgs a;
+  a.k = k.ptr; a.k_sb = k.stride_b; a.k_st = k.stride_t; a.k_sh = k.stride_h;
+  a.pyr = pyr;
+  a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.head_dim = cfg->head_dim; a.n = n;
+  a.bf16 = cfg->dtype == PISA_BF16;
+  a.lv = make_levels(n, capacity);
+  return hip_status(pisa::launch_pyramid(a, (hipStream_t)stream));
+}
+
+size_t pisa_select_workspace_bytes(const pisa_cfg* cfg) {
+  if (check_cfg(cfg) != PISA_OK) return 0;
+  return select_layout(cfg).total;
+}
+
+pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr, int32_t* sel,
+                               float* sel_u, void* ws, size_t ws_bytes, void* stream) {
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  if (cfg->seq_len > kMaxSeqSelect) return PISA_ERR_UNSUPPORTED;
+  if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
+  if (!aligned16(pyr) || !sel) return PISA_ERR_INVALID_ARG;
+  const SelectWorkspace w = select_layout(cfg);
+  if (!ws || ws_bytes < w.total || ((uintptr_t)ws & 255u)) return PISA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  int32_t* cand = reinterpret_cast<int32_t*>(base + w.cand);
+  float* leaf_u = reinterpret_cast<float*>(base + w.leaf_u);
+  int32_t* pairs = reinterpret_cast<int32_t*>(base + w.pairs);
+  int32_t* leaf_off = reinterpret_cast<int32_t*>(base + w.leaf_off);
+  const int N = cfg->seq_len, G = cfg->n_q_heads / cfg->n_kv_heads, width = 2 * cfg->top_k;
+  const int m1 = (N + pisa::kLeaf - 1) / pisa::kLeaf;
+  const bool bf16 = cfg->dtype == PISA_BF16;
+  const float scale = resolve_scale(cfg);
+  hipStream_t s = (hipStream_t)stream;
+
+  pisa::RouteArgs r;
+  r.q = q.ptr; r.q_sb = q.stride_b; r.q_st = q.stride_t; r.q_sh = q.stride_h;
+  r.pyr = pyr; r.cand = cand;
+  r.batch = cfg->batch; r.n_kv_heads = cfg->n_kv_heads; r.group = G; r.head_dim = cfg->head_dim;
+  r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16;
+  r.lv = make_levels(N, N);
+  if ((st = hip_status(pisa::launch_route(r, s))) != PISA_OK) return st;
+
+  pisa::ClusterArgs c;
+  c.cand = cand; c.pairs = pairs; c.leaf_off = leaf_off;
+  c.batch = cfg->batch; c.n_kv_heads = cfg->n_kv_heads; c.n = N; c.width = width;
+  c.n_leaves = m1; c.window = kWindow; c.n_windows = w.n_windows;
+  if ((st = hip_status(pisa::launch_cluster(c, s))) != PISA_OK) return st;
+
+  pisa::LeafArgs l;
+  l.q = q.ptr; l.q_sb = q.stride_b; l.q_st = q.stride_t; l.q_sh = q.stride_h;
+  l.k = k.ptr; l.k_sb = k.stride_b; l.k_st = k.stride_t; l.k_sh = k.stride_h;
+  l.pairs = pairs; l.leaf_off = leaf_off; l.leaf_u = leaf_u;
+  l.batch = cfg->batch; l.n_kv_heads = cfg->n_kv_heads; l.group = G; l.head_dim = cfg->head_dim;
+  l.n = N; l.width = width; l.n_leaves = m1; l.window = kWindow; l.n_windows = w.n_windows;
+  l.scale = scale; l.bf16 = bf16;
+  if ((st = hip_status(pisa::launch_leaf_lse(l, s))) != PISA_OK) return st;
+
+  pisa::TopkArgs t;
+  t.cand = cand; t.leaf_u = leaf_u; t.sel = sel; t.sel_u = sel_u;
+  t.batch = cfg->batch; t.n_kv_heads = cfg->n_kv_heads; t.n = N; t.width = width; t.top_k = cfg->top_k;
+  return hip_status(pisa::launch_topk(t, s));
+}
+
+pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                 const int32_t* sel, pisa_tensor_mut o, float* row_lse, void* stream) {
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(v.ptr, v.stride_b, v.stride_t, v.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(o.ptr, o.stride_b, o.stride_t, o.stride_h)) != PISA_OK) return st;
+  if (!sel) return PISA_ERR_INVALID_ARG;
+  pisa::AttnArgs a;
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_st = q.stride_t; a.q_sh = q.stride_h;
+  a.k = k.ptr; a.k_sb = k.stride_b; a.k_st = k.stride_t; a.k_sh = k.stride_h;
+  a.v = v.ptr; a.v_sb = v.stride_b; a.v_st = v.stride_t; a.v_sh = v.stride_h;
+  a.sel = sel;
+  a.o = o.ptr; a.o_sb = o.stride_b; a.o_st = o.stride_t; a.o_sh = o.stride_h;
+  a.row_lse = row_lse;
+  a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
+  a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  return hip_status(pisa::launch_attention(a, (hipStream_t)stream));
+}
+
+pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
+                             pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache, float* pyr,
+                             int32_t* sel_out, pisa_tensor_mut o, void* stream) {
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  const int G = cfg->n_q_heads / cfg->n_kv_heads;
+  if (n_ctx < 0 || n_ctx + 1 > cfg->seq_len) return PISA_ERR_INVALID_ARG;
+  if (G * 2 * cfg->top_k > 256) return PISA_ERR_UNSUPPORTED;
+  if ((st = check_tensor(q.ptr, q.stride_b, 0, q.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(k_new.ptr, k_new.stride_b, 0, k_new.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(v_new.ptr, v_new.stride_b, 0, v_new.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(k_cache.ptr, k_cache.stride_b, k_cache.stride_t, k_cache.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(v_cache.ptr, v_cache.stride_b, v_cache.stride_t, v_cache.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(o.ptr, o.stride_b, 0, o.stride_h)) != PISA_OK) return st;
+  if (!aligned16(pyr)) return PISA_ERR_INVALID_ARG;
+  pisa::DecodeArgs a;
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_sh = q.stride_h;
+  a.k_new = k_new.ptr; a.kn_sb = k_new.stride_b; a.kn_sh = k_new.stride_h;
+  a.v_new = v_new.ptr; a.vn_sb = v_new.stride_b; a.vn_sh = v_new.stride_h;
+  a.k_cache = k_cache.ptr; a.kc_sb = k_cache.stride_b; a.kc_st = k_cache.stride_t; a.kc_sh = k_cache.stride_h;
+  a.v_cache = v_cache.ptr; a.vc_sb = v_cache.stride_b; a.vc_st = v_cache.stride_t; a.vc_sh = v_cache.stride_h;
+  a.pyr = pyr; a.sel_out = sel_out;
+  a.o = o.ptr; a.o_sb = o.stride_b; a.o_sh = o.stride_h;
+  a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = G; a.head_dim = cfg->head_dim;
+  a.top_k = cfg->top_k; a.n_ctx = n_ctx; a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  a.lv = make_levels(n_ctx + 1, cfg->seq_len);
+  return hip_status(pisa::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

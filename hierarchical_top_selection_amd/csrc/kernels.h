@@ -1,0 +1,109 @@
+// kernels.h - host-visible argument blocks and launchers of the gfx950 kernels.
+// Strides are in elements; every launcher enqueues on the given stream and
+// returns the launch status (nothing is synchronised).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pisa_device.h"
+
+namespace pisa {
+
+struct PyramidArgs {
+  const void* k;
+  int64_t k_sb, k_st, k_sh;
+  float* pyr;
+  int batch, n_kv_heads, head_dim, n;
+  bool bf16;
+  Levels lv;          // sizes for length n, offsets for the capacity layout
+};
+
+struct RouteArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  const float* pyr;
+  int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
+  int batch, n_kv_heads, group, head_dim, n, top_k;
+  float scale;
+  bool bf16;
+  Levels lv;
+};
+
+struct ClusterArgs {
+  const int32_t* cand;   // [B*Hkv][N][2K]
+  int32_t* pairs;        // [B*Hkv][N][2K] packed (t << 6 | slot), grouped by leaf per window
+  int32_t* leaf_off;     // [B*Hkv][n_windows][M1 + 1]
+  int batch, n_kv_heads, n, width, n_leaves, window, n_windows;
+};
+
+struct LeafArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  const void* k;
+  int64_t k_sb, k_st, k_sh;
+  const int32_t* pairs;
+  const int32_t* leaf_off;
+  float* leaf_u;         // [B*Hkv][N][2K]
+  int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows;
+  float scale;
+  bool bf16;
+};
+
+struct TopkArgs {
+  const int32_t* cand;
+  const float* leaf_u;
+  int32_t* sel;          // [B*Hkv][N][K]
+  float* sel_u;          // optional
+  int batch, n_kv_heads, n, width, top_k;
+};
+
+struct AttnArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  const void* k;
+  int64_t k_sb, k_st, k_sh;
+  const void* v;
+  int64_t v_sb, v_st, v_sh;
+  const int32_t* sel;
+  void* o;
+  int64_t o_sb, o_st, o_sh;
+  float* row_lse;        // optional [B][Hq][N]
+  int batch, n_kv_heads, group, head_dim, n, top_k;
+  float scale;
+  bool bf16;
+};
+
+struct DecodeArgs {
+  const void* q;            // [B][Hq][d]
+  int64_t q_sb, q_sh;
+  const void* k_new;
+  int64_t kn_sb, kn_sh;
+  const void* v_new;
+  int64_t vn_sb, vn_sh;
+  void* k_cache;
+  int64_t kc_sb, kc_st, kc_sh;
+  void* v_cache;
+  int64_t vc_sb, vc_st, vc_sh;
+  float* pyr;
+  int32_t* sel_out;         // optional [B][Hkv][K]
+  void* o;                  // [B][Hq][d]
+  int64_t o_sb, o_sh;
+  int batch, n_kv_heads, group, head_dim, top_k, n_ctx;
+  float scale;
+  bool bf16;
+  Levels lv;                // sizes for length n_ctx + 1, capacity offsets
+};
+
+hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
+hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// LDS bytes of the fused decode kernel for (group, 2K, d).
+size_t decode_lds_bytes(int group, int width, int head_dim);
+
+}  // namespace pisa

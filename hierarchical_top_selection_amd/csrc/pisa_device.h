@@ -1,0 +1,147 @@
+// pisa_device.h - device-side building blocks shared by the gfx950 kernels.
+//
+// MFMA operand layout (verified on gfx950 for v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32): lane l of the wave supplies row (l % 16) of the
+// 16-row A tile and column (l % 16) of the 16-column B tile, covering the
+// k-slice owned by its lane group g = l / 16; the 16x16 fp32 result gives
+// lane l column (l % 16) and rows 4 * g + i, i = 0..3.  Because A and B use
+// the same k-slice per lane, any bijection between (k-step, g) and the
+// contraction index is valid as long as both operands use it; the loaders
+// below pick the bijection that makes each lane's loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+constexpr int kLeaf = 64;      // C: keys per leaf block
+constexpr int kFanout = 2;     // g: children per node above the leaves
+constexpr int kMaxLevels = 32;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------- geometry
+// Level sizes for the current length and node offsets for the capacity layout.
+struct Levels {
+  int count;                   // levels for the current length: L(n)
+  int size[kMaxLevels];        // size[l-1] = M_l(n)
+  int64_t offset[kMaxLevels];  // node offset of level l in the capacity layout
+  int64_t nodes;               // nodes per (b, kvh) in the capacity layout
+};
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// First key covered by node i of level l (level 1 = leaves).
+__device__ inline int64_t node_first_key(int level, int64_t i) {
+  return i * (int64_t)kLeaf << (level - 1);
+}
+
+// ----------------------------------------------------------------------------- element I/O
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // RNE
+
+// Four consecutive elements starting at p (p 8-byte aligned for bf16, 16-byte for f32).
+__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 load4(const __bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
+// ----------------------------------------------------------------------------- MFMA fragments
+// Row fragment of a 16 x D operand tile for the fp32 MFMA (16x16x4): the lane
+// holds, for m = 0..D/16-1, the four contraction indices 16 m + 4 g + j, which
+// feed k-steps 4 m + j.
+template <int D>
+struct FragF32 {
+  float4 v[D / 16];
+  template <typename T>
+  __device__ inline void load(const T* row, int g) {
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) v[m] = load4(row + 16 * m + 4 * g);
+  }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) v[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+};
+
+// Row fragment for the bf16 MFMA (16x16x32): k-step s covers indices 32 s + 8 g + j.
+template <int D>
+struct FragBF16 {
+  bf16x8 v[D / 32];
+  __device__ inline void load(const __bf16* row, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) v[s] = *reinterpret_cast<const bf16x8*>(row + 32 * s + 8 * g);
+  }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[s][j] = (__bf16)0.f;
+  }
+};
+
+__device__ inline floatx4 mfma_f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += A(16 x D) * B(D x 16) with both operands as row fragments.
+template <int D>
+__device__ inline floatx4 mma(const FragF32<D>& a, const FragF32<D>& b, floatx4 acc) {
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) {
+    acc = mfma_f32(a.v[m].x, b.v[m].x, acc);
+    acc = mfma_f32(a.v[m].y, b.v[m].y, acc);
+    acc = mfma_f32(a.v[m].z, b.v[m].z, acc);
+    acc = mfma_f32(a.v[m].w, b.v[m].w, acc);
+  }
+  return acc;
+}
+template <int D>
+__device__ inline floatx4 mma(const FragBF16<D>& a, const FragBF16<D>& b, floatx4 acc) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) acc = mfma_bf16(a.v[s], b.v[s], acc);
+  return acc;
+}
+
+// Fragment type used for raw Q/K contractions of element type T.
+template <typename T, int D> struct RawFrag;
+template <int D> struct RawFrag<float, D> { typedef FragF32<D> type; };
+template <int D> struct RawFrag<__bf16, D> { typedef FragBF16<D> type; };
+
+// ----------------------------------------------------------------------------- wave reductions
+__device__ inline float wave_max_xor(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask, 64)); }
+__device__ inline float wave_add_xor(float x, int mask) { return x + __shfl_xor(x, mask, 64); }
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes' data
+// (wave-private staging buffers; no workgroup barrier needed).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Index of the p-th set bit (p counted from 0) of a non-empty 64-bit mask.
+__device__ inline int nth_set_bit(uint64_t mask, int p) {
+  int pos = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+    const int k = pos + step;
+    const uint64_t below = k >= 64 ? mask : (mask & ((1ull << k) - 1ull));
+    if (__popcll(below) <= p) pos = k;
+  }
+  return pos;
+}
+
+}  // namespace pisa

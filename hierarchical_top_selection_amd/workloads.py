@@ -127,29 +127,50 @@ def planted_blocks(w: Workload, b: int, kvh: int, n_leaves: int | None = None) -
     return np.sort(_rng(w.seed, 98, b, kvh).choice(m1, min(w.plant_blocks, m1), replace=False))
 
 
-def q_slice(w: Workload, b: int, h: int, n: int | None = None) -> np.ndarray:
-    """Q[b, :n, h, :] as float32 values already rounded to the workload dtype."""
-    n = w.seq_len if n is None else n
+def _draw_q(w: Workload, b: int, h: int, n: int) -> np.ndarray:
     x = _rng(w.seed, 0, b, h).standard_normal((n, w.head_dim), dtype=np.float32)
     if w.alpha_q:
         x += np.float32(w.alpha_q) * planted_direction(w)
-    return quantise(x, w.dtype)
+    return x
 
 
-def k_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
-    n = w.seq_len if n is None else n
+def _draw_k(w: Workload, b: int, kvh: int, n: int) -> np.ndarray:
     x = _rng(w.seed, 1, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
     if w.plant_blocks:
         shift = np.float32(w.alpha_k) * planted_direction(w)
         for j in planted_blocks(w, b, kvh, -(-n // w.block)):
             x[j * w.block:(j + 1) * w.block] += shift
-    return quantise(x, w.dtype)
+    return x
+
+
+def _draw_v(w: Workload, b: int, kvh: int, n: int) -> np.ndarray:
+    return _rng(w.seed, 2, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
+
+
+_DRAW = {"q": _draw_q, "k": _draw_k, "v": _draw_v}
+
+
+def draw(w: Workload, which: str, b: int, h: int, n: int | None = None, bits: bool = False) -> np.ndarray:
+    """One [n, d] slice of Q ('q', head h) or K / V ('k' / 'v', KV head h) of sequence b.
+
+    Returns float32 values rounded to the workload dtype, or with ``bits`` the
+    storage form (float32 for fp32 workloads, uint16 bfloat16 patterns otherwise).
+    """
+    x = _DRAW[which](w, b, h, w.seq_len if n is None else n)
+    return to_storage(x, w.dtype) if bits else quantise(x, w.dtype)
+
+
+def q_slice(w: Workload, b: int, h: int, n: int | None = None) -> np.ndarray:
+    """Q[b, :n, h, :] as float32 values already rounded to the workload dtype."""
+    return draw(w, "q", b, h, n)
+
+
+def k_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
+    return draw(w, "k", b, kvh, n)
 
 
 def v_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
-    n = w.seq_len if n is None else n
-    x = _rng(w.seed, 2, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
-    return quantise(x, w.dtype)
+    return draw(w, "v", b, kvh, n)
 
 
 def decode_tokens(w: Workload, which: str, b: int, h: int) -> np.ndarray:
@@ -159,23 +180,33 @@ def decode_tokens(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     return quantise(x, w.dtype)
 
 
-def prefill_inputs(w: Workload, batches=None, n: int | None = None):
-    """Full Q [B, n, Hq, d], K and V [B, n, Hkv, d] as float32 arrays (values in the workload dtype).
+def prefill_inputs(w: Workload, batches=None, n: int | None = None, bits: bool = False, threads: int = 8,
+                   with_q: bool = True):
+    """Q [B, n, Hq, d], K and V [B, n, Hkv, d] for the given sequences (default: all).
 
-    ``batches`` restricts generation to a subset of sequence indices (the
-    arrays then hold those sequences in order); ``n`` truncates the length.
+    float32 values in the workload dtype, or storage arrays with ``bits``
+    (uint16 bfloat16 patterns for bf16 workloads).  Slices are drawn in a
+    thread pool; every slice comes from its own seeded stream, so the result
+    does not depend on the pool.
     """
+    import concurrent.futures
+
     batches = list(range(w.batch)) if batches is None else list(batches)
     n = w.seq_len if n is None else n
-    q = np.empty((len(batches), n, w.n_q_heads, w.head_dim), dtype=np.float32)
-    k = np.empty((len(batches), n, w.n_kv_heads, w.head_dim), dtype=np.float32)
+    dt = (np.uint16 if w.dtype == "bf16" else np.float32) if bits else np.float32
+    q = np.empty((len(batches), n, w.n_q_heads if with_q else 0, w.head_dim), dtype=dt)
+    k = np.empty((len(batches), n, w.n_kv_heads, w.head_dim), dtype=dt)
     v = np.empty_like(k)
-    for bi, b in enumerate(batches):
-        for h in range(w.n_q_heads):
-            q[bi, :, h] = q_slice(w, b, h, n)
-        for h in range(w.n_kv_heads):
-            k[bi, :, h] = k_slice(w, b, h, n)
-            v[bi, :, h] = v_slice(w, b, h, n)
+    jobs = [(q, "q", bi, b, h) for bi, b in enumerate(batches) for h in range(q.shape[2])]
+    jobs += [(arr, name, bi, b, h) for bi, b in enumerate(batches) for h in range(w.n_kv_heads)
+             for arr, name in ((k, "k"), (v, "v"))]
+
+    def run(job):
+        arr, name, bi, b, h = job
+        arr[bi, :, h] = draw(w, name, b, h, n, bits=bits)
+
+    with concurrent.futures.ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(run, jobs))
     return q, k, v
 
 

@@ -1,0 +1,181 @@
+/*
+ * pisa.h - C ABI of the MI355X (gfx950) PISA hot path: key pyramid, hierarchical
+ * LogSumExp block selection, block-sparse attention and the decode step.
+ *
+ * The method is the one described on the paper-summary page "Block Sparse
+ * Attention with Log-Linear Complexity" (Tang, Qin, Pan, Li, Liu).  Section
+ * names below refer to that page: Prerequisites (block sparse attention,
+ * LogSumExp, grouped-query attention), Core method (pyramid eq. 10-15,
+ * routing eq. 16-20, LSE score eq. 21) and Method steps (pyramid mean,
+ * Stage 1 head sum eq. 22, Stage 2 leaf LSE, final top-K, decode update,
+ * attention on the selected leaves).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps device memory and never synchronises the
+ *    stream: every call only validates its arguments on the host and enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*; NULL = default
+ *    stream).  Inputs must stay alive until the stream has passed the call.
+ *  - Token-major tensors (Q, K, V, O, KV caches) are described by pisa_tensor:
+ *    element [b][t][h][c] lives at ptr + b*stride_b + t*stride_t + h*stride_h + c
+ *    (strides in ELEMENTS, the head_dim axis contiguous).  The pointer must be
+ *    16-byte aligned and every stride a multiple of 8 elements.
+ *  - GQA: query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads
+ *    (contiguous groups).
+ *  - The pyramid is float32, [batch][n_kv_heads][nodes(capacity)][head_dim],
+ *    levels stored leaf level first: level 1 (leaves, M_1 = ceil(cap / 64)
+ *    nodes) at node offset 0, then level 2 (M_2 = ceil(M_1 / 2) nodes), ...,
+ *    up to the level with one node.  For a current length n <= capacity only
+ *    the first ceil(n / 64), ceil(ceil(n/64)/2), ... nodes of each level are
+ *    meaningful; the root of length n is node 0 of level L(n).
+ *  - Selections are int32 [batch][n_kv_heads][tokens][top_k]: leaf-block ids in
+ *    ascending order, padded with -1.  Block j covers keys [64 j, 64 j + 64).
+ *  - Errors: arguments are checked before anything is enqueued; a non-zero
+ *    pisa_status means nothing was launched, except PISA_ERR_HIP, which means a
+ *    launch failed (pisa_last_hip_error() then returns the hipError_t value of
+ *    the calling thread's last failure).  No C++ exception crosses the ABI.
+ *  - Thread safety: no global mutable state besides the thread-local error code.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PISA_ABI_VERSION 1
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misaligned pointer or stride */
+  PISA_ERR_UNSUPPORTED = 2,   /* valid request outside the supported envelope */
+  PISA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than required */
+  PISA_ERR_HIP = 4            /* a kernel launch failed */
+} pisa_status;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+/*
+ * Problem description.  Supported envelope: block == 64 (C), fanout == 2 (g),
+ * head_dim in {64, 128}, n_q_heads % n_kv_heads == 0 with G = n_q_heads /
+ * n_kv_heads in {1, 2, 4, 8, 16}, 1 <= top_k <= 32, seq_len >= 1 and
+ * seq_len * 2 * top_k < 2^31.  scale <= 0 selects 1/sqrt(head_dim), the scale
+ * of the LSE score (Core method, eq. 21), also used by attention.
+ */
+typedef struct {
+  int32_t batch;        /* B */
+  int32_t seq_len;      /* N for prefill; KV-cache capacity for decode */
+  int32_t n_q_heads;    /* H_q */
+  int32_t n_kv_heads;   /* H_kv */
+  int32_t head_dim;     /* d */
+  int32_t block;        /* C, leaf block size: must be 64 */
+  int32_t fanout;       /* g, children per node above the leaves: must be 2 */
+  int32_t top_k;        /* K, leaf blocks kept per (token, KV head) */
+  pisa_dtype dtype;     /* element type of Q, K, V, O and the KV caches */
+  float scale;          /* logit scale; <= 0 means 1/sqrt(head_dim) */
+} pisa_cfg;
+
+typedef struct { const void* ptr; int64_t stride_b, stride_t, stride_h; } pisa_tensor;
+typedef struct { void* ptr; int64_t stride_b, stride_t, stride_h; } pisa_tensor_mut;
+
+/* ABI version of the loaded library (PISA_ABI_VERSION). */
+int pisa_abi_version(void);
+
+/* Static description of a status code. */
+const char* pisa_status_string(pisa_status status);
+
+/* hipError_t of the calling thread's last failed launch (0 if none). */
+int pisa_last_hip_error(void);
+
+/* Nodes per (sequence, KV head) of a pyramid with room for `capacity` keys:
+ * sum over levels of ceil(capacity / 64), then repeated ceil(/2) down to 1.
+ * Returns 0 for capacity < 1. */
+int64_t pisa_pyramid_nodes(int32_t capacity);
+
+/* Bytes of a pyramid for cfg->batch * cfg->n_kv_heads sequences of `capacity` keys. */
+size_t pisa_pyramid_bytes(const pisa_cfg* cfg, int32_t capacity);
+
+/*
+ * build_pyramid - mean-pooled key pyramid (Method steps, first step; Core
+ * method eq. 10-15).  Leaf i of each (b, kvh) is the float32 mean of keys
+ * [64 i, min(64 i + 64, n)) summed in key order; a node above is the mean of
+ * its one or two children, (c0 + c1) * 0.5 (the unweighted mean, also for
+ * partial nodes).  Writes levels for length n into `pyr`, laid out for
+ * `capacity` (>= n) keys as described above.
+ *   k    : [B][>= n][H_kv][d] keys, cfg->dtype
+ *   pyr  : float32 output, pisa_pyramid_bytes(cfg, capacity) bytes
+ */
+pisa_status pisa_build_pyramid(const pisa_cfg* cfg, pisa_tensor k, int32_t n, int32_t capacity,
+                               float* pyr, void* stream);
+
+/* Workspace bytes needed by pisa_select_blocks for cfg (256-byte aligned pieces). */
+size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
+
+/*
+ * select_blocks - hierarchical top-K leaf selection for every query token t
+ * in [0, N) of every (b, kvh) (Core method eq. 16-21; Method steps eq. 22 and
+ * the two selection stages).  From the root, each level with more than K
+ * candidates scores every candidate by u = sum over the group's query heads of
+ * the LSE of the head's scaled dot products with the candidate's causally
+ * valid children (node (l, i) is valid for t when its first key
+ * i * 64 * 2^(l-1) <= t), keeps K by (u descending, index ascending) and
+ * expands the survivors to their valid children.  The leaf level scores the
+ * at most 2K candidate leaves exactly over their raw keys at positions <= t.
+ *   q, k    : [B][N][H_q][d] and [B][N][H_kv][d], cfg->dtype
+ *   pyr     : pyramid of k built with n = N (capacity N)
+ *   sel     : int32 [B][H_kv][N][K] output, ascending, -1 padded
+ *   sel_u   : optional float32 [B][H_kv][N][K] output (NULL to skip): the leaf
+ *             score u of each selected block, -inf on padding
+ *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes; its
+ *             first B*H_kv*N*2K int32 hold the leaf candidates of each token
+ *             (-1 padded) after the call
+ */
+pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
+                               int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_attn_fwd - causal softmax attention of each query head over the raw
+ * keys/values of its group's selected blocks (Prerequisites, block sparse
+ * attention; Method steps, fourth step): the key set of token t is the union
+ * of blocks in sel[b][kvh][t] cut to positions <= t; fp32 accumulation.
+ *   q, k, v : cfg->dtype, shapes as in select_blocks (v like k)
+ *   sel     : int32 [B][H_kv][N][K] (any entry < 0 ends nothing: it is skipped;
+ *             valid entries must satisfy 64 * j <= t, else the result for that
+ *             token is unspecified)
+ *   o       : [B][N][H_q][d] output, cfg->dtype
+ *   row_lse : optional float32 [B][H_q][N] output (NULL to skip): natural-log
+ *             normaliser of each row's softmax
+ */
+pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                 const int32_t* sel, pisa_tensor_mut o, float* row_lse, void* stream);
+
+/*
+ * decode_step - one autoregressive step for every sequence (Method steps,
+ * third step): writes k_new / v_new at position n_ctx of the caches, updates
+ * the leaf n_ctx / 64 and its ancestor path in `pyr` (same arithmetic and
+ * order as build_pyramid, so the result equals a rebuild at length n_ctx + 1),
+ * then routes the new query at t = n_ctx (every key valid) through all levels
+ * with exact leaf LSE in one fused kernel and attends over the selected blocks.
+ *   cfg->seq_len      : cache capacity; requires n_ctx + 1 <= capacity
+ *   n_ctx             : keys already in the cache (same for every sequence)
+ *   q                 : [B][H_q][d]    (stride_t ignored)
+ *   k_new, v_new      : [B][H_kv][d]   (stride_t ignored)
+ *   k_cache, v_cache  : [B][capacity][H_kv][d], updated in place
+ *   pyr               : pyramid of the cache (capacity layout), updated in place
+ *   sel_out           : optional int32 [B][H_kv][K] (NULL to skip)
+ *   o                 : [B][H_q][d] output (stride_t ignored)
+ * Requires G * 2K <= 256 (leaf logits are staged on chip).
+ */
+pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
+                             pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache,
+                             float* pyr, int32_t* sel_out, pisa_tensor_mut o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

@@ -311,30 +311,33 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, K: int, C: int = 64, g:
 
 
 class DecodeState:
-    """KV cache and pyramid of one (sequence, KV head) for the decode oracle [Steps: third step]."""
+    """KV cache and pyramid of one (sequence, KV head) for the decode oracle [Steps: third step].
 
-    def __init__(self, k: np.ndarray, v: np.ndarray, C: int = 64, g: int = 2):
-        self.k = [np.asarray(k, dtype=np.float64)]
-        self.v = [np.asarray(v, dtype=np.float64)]
+    The cache is preallocated for ``capacity`` keys; ``n`` keys are present.
+    """
+
+    def __init__(self, k: np.ndarray, v: np.ndarray, C: int = 64, g: int = 2, capacity: int | None = None):
+        n, d = k.shape
+        capacity = n + 1024 if capacity is None else capacity
+        self.kbuf = np.zeros((capacity, d))
+        self.vbuf = np.zeros((capacity, d))
+        self.kbuf[:n] = k
+        self.vbuf[:n] = v
         self.C, self.g = C, g
-        self.n = k.shape[0]
-        self.pyr = build_pyramid(self.k[0], C, g) if self.n else []
+        self.n = n
+        self.pyr = build_pyramid(self.kbuf[:n], C, g) if n else []
 
     def keys(self) -> np.ndarray:
-        if len(self.k) > 1:
-            self.k = [np.concatenate(self.k)]
-        return self.k[0]
+        return self.kbuf[:self.n]
 
     def values(self) -> np.ndarray:
-        if len(self.v) > 1:
-            self.v = [np.concatenate(self.v)]
-        return self.v[0]
+        return self.vbuf[:self.n]
 
     def step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, K: int,
              scale: float | None = None):
         """Append (k_new, v_new) at position n, update the pyramid, route q at t = n, attend (R6)."""
-        self.k.append(np.asarray(k_new, dtype=np.float64)[None, :])
-        self.v.append(np.asarray(v_new, dtype=np.float64)[None, :])
+        self.kbuf[self.n] = k_new
+        self.vbuf[self.n] = v_new
         self.n += 1
         keys = self.keys()
         self.pyr = update_pyramid(self.pyr, keys, self.n, self.C, self.g)

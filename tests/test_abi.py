@@ -1,0 +1,87 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol that
+include/pisa.h declares, sizes pyramids and workspaces, and rejects invalid
+arguments before launching anything (no kernel runs in these tests)."""
+import ctypes
+
+import pytest
+
+from hierarchical_top_selection_amd import binding
+from oracle import pisa as oracle
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = binding.header_symbols()
+    assert len(declared) == 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.pisa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.pisa_status_string(0).decode() == "ok"
+    assert "unsupported" in lib.pisa_status_string(2).decode()
+
+
+@pytest.mark.parametrize("cap", [1, 63, 64, 65, 1024, 4096, 131072, 131328, 262144])
+def test_pyramid_nodes_match_level_sizes(lib, cap):
+    assert lib.pisa_pyramid_nodes(cap) == sum(oracle.level_sizes(cap))
+
+
+def test_pyramid_nodes_rejects_empty(lib):
+    assert lib.pisa_pyramid_nodes(0) == 0
+
+
+def _cfg(**kw):
+    base = dict(batch=1, seq_len=4096, n_q_heads=16, n_kv_heads=1, head_dim=128, top_k=16, dtype=None)
+    base.update(kw)
+    import torch
+    return binding.make_cfg(base["batch"], base["seq_len"], base["n_q_heads"], base["n_kv_heads"],
+                            base["head_dim"], base["top_k"], base["dtype"] or torch.bfloat16)
+
+
+def test_workspace_and_pyramid_bytes(lib):
+    cfg = _cfg(batch=2, seq_len=32768, n_q_heads=32, n_kv_heads=2, top_k=32)
+    slots = 2 * 2 * 32768 * 64
+    ws = lib.pisa_select_workspace_bytes(ctypes.byref(cfg))
+    assert ws >= 3 * slots * 4
+    assert lib.pisa_pyramid_bytes(ctypes.byref(cfg), 32768) == 2 * 2 * sum(oracle.level_sizes(32768)) * 128 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, 2), ("top_k", 33, 2), ("top_k", 0, 1), ("n_kv_heads", 5, 1), ("n_q_heads", 24, 2),
+    ("block", 32, 2), ("fanout", 4, 2), ("seq_len", 0, 1), ("batch", 0, 1), ("dtype", 7, 1),
+])
+def test_invalid_configs_are_rejected_before_launch(lib, field, value, status):
+    cfg = _cfg()
+    setattr(cfg, field, value)
+    t = binding.PisaTensor(16, 0, 128, 128)
+    got = lib.pisa_build_pyramid(ctypes.byref(cfg), t, 16, 16, ctypes.c_void_p(16), None)
+    assert got == status
+    assert lib.pisa_select_workspace_bytes(ctypes.byref(cfg)) == 0
+
+
+def test_invalid_tensors_are_rejected_before_launch(lib):
+    cfg = _cfg()
+    good = binding.PisaTensor(4096, 0, 128, 128)
+    assert lib.pisa_build_pyramid(ctypes.byref(cfg), binding.PisaTensor(None, 0, 128, 128), 16, 16,
+                                  ctypes.c_void_p(4096), None) == 1          # null
+    assert lib.pisa_build_pyramid(ctypes.byref(cfg), binding.PisaTensor(4100, 0, 128, 128), 16, 16,
+                                  ctypes.c_void_p(4096), None) == 1          # misaligned
+    assert lib.pisa_build_pyramid(ctypes.byref(cfg), binding.PisaTensor(4096, 0, 130, 128), 16, 16,
+                                  ctypes.c_void_p(4096), None) == 1          # stride not a multiple of 8
+    assert lib.pisa_build_pyramid(ctypes.byref(cfg), good, 17, 16, ctypes.c_void_p(4096), None) == 1   # n > capacity
+    # workspace too small
+    assert lib.pisa_select_blocks(ctypes.byref(cfg), good, good, ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                                  None, ctypes.c_void_p(4096), 16, None) == 3
+    # decode: position beyond capacity, and the on-chip limit G * 2K <= 256
+    o = binding.PisaTensor(4096, 0, 0, 128)
+    assert lib.pisa_decode_step(ctypes.byref(cfg), 4096, good, good, good, good, good, ctypes.c_void_p(4096),
+                                None, o, None) == 1
+    big = _cfg(top_k=16, n_q_heads=16)
+    assert lib.pisa_decode_step(ctypes.byref(big), 10, good, good, good, good, good, ctypes.c_void_p(4096),
+                                None, o, None) == 2

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs.  See tests/gpu_harness.py for the comparison rules."""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_top_selection_amd import binding
+from hierarchical_top_selection_amd import workloads as W
+from oracle import pisa as oracle
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _pyramid_levels(flat: np.ndarray, n: int, capacity: int):
+    """Split a capacity-layout pyramid [nodes, d] into the levels of length n."""
+    cap_sizes = oracle.level_sizes(capacity)
+    sizes = oracle.level_sizes(n)
+    out, off = [], 0
+    for lvl, cap in enumerate(cap_sizes):
+        if lvl < len(sizes):
+            out.append(flat[off:off + sizes[lvl]])
+        off += cap
+    return out
+
+
+def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: int = 0):
+    B, N, G, K = w.batch, w.seq_len, w.group, w.top_k
+    H.log(f"[{label}] inputs B={B} N={N} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} K={K} {w.dtype}")
+    q, k, v = W.prefill_inputs(w, bits=True)
+    H.log(f"[{label}] GPU pyramid + select + attention")
+    g = H.run_gpu_prefill(w, q, k, v)
+    pyr = g["pyr"].cpu().numpy()
+    sel = g["sel"].cpu().numpy()
+    sel_u = g["sel_u"].cpu().numpy()
+    o = g["o"].float().cpu().numpy()
+    sel_in = g["sel"].clone()
+    n_bad = n_total = 0
+    units = []
+    max_du = 0.0
+    for b in range(B):
+        for kvh in range(w.n_kv_heads):
+            ts = np.arange(N) if sample is None else H.sample_tokens(N, sample, seed + 7 * b + kvh)
+            H.log(f"[{label}] oracle b={b} kvh={kvh} on {len(ts)} tokens")
+            ora = H.oracle_prefill(w, q, k, v, b, kvh, ts)
+            # pyramid: fp32 sums in key order vs the fp64 mean
+            kk = H.host_values(k[b, :, kvh]).astype(np.float64)
+            for got, want in zip(_pyramid_levels(pyr[b, kvh], N, N), oracle.build_pyramid(kk)):
+                np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-5)
+            nb, agree = H.compare_selection(sel[b, kvh, ts], ora["sel"], ora["gap"], label)
+            n_bad += nb
+            n_total += len(ts)
+            # exact leaf scores of the selected leaves (rows that agree)
+            qg = H.host_values(q[b, :, kvh * G:(kvh + 1) * G]).astype(np.float64)
+            for r in np.nonzero(agree)[0][:: max(1, len(ts) // 200)]:
+                t = int(ts[r])
+                for slot, j in enumerate(ora["sel"][r]):
+                    if j < 0:
+                        continue
+                    want = float(np.sum(oracle.leaf_lse(qg[t], kk, int(j), t)))
+                    du = abs(float(sel_u[b, kvh, t, slot]) - want)
+                    max_du = max(max_du, du)
+                    assert du <= 1e-4 + 1e-5 * abs(want), (label, t, j, sel_u[b, kvh, t, slot], want)
+            # end-to-end attention where the selections agree
+            heads = slice(kvh * G, (kvh + 1) * G)
+            tol_abs, tol_rel = H.attn_tolerance(w)
+            ma, rl = H.attn_errors(o[b, ts][:, heads][agree], ora["o"][agree])
+            assert ma <= tol_abs and rl <= tol_rel, (label, "end-to-end", ma, rl)
+            sel_in[b, kvh, torch.from_numpy(ts).to(H.DEV)] = torch.from_numpy(ora["sel"].astype(np.int32)).to(H.DEV)
+            units.append((b, kvh, ts, ora))
+    H.assert_mismatch_budget(n_bad, n_total, label)
+    H.log(f"[{label}] max |du| on selected leaves {max_du:.3g}")
+    # attention on the oracle's own selection (fed to the kernel as input)
+    o2, lse2 = binding.sparse_attn_fwd(g["q"], g["k"], g["v"], sel_in, return_lse=True)
+    o2 = o2.float().cpu().numpy()
+    lse2 = lse2.cpu().numpy()
+    worst = (0.0, 0.0)
+    for b, kvh, ts, ora in units:
+        heads = slice(kvh * G, (kvh + 1) * G)
+        ma, rl = H.attn_errors(o2[b, ts][:, heads], ora["o"])
+        worst = (max(worst[0], ma), max(worst[1], rl))
+        tol_abs, tol_rel = H.attn_tolerance(w)
+        assert ma <= tol_abs and rl <= tol_rel, (label, b, kvh, ma, rl)
+        np.testing.assert_allclose(lse2[b, heads][:, ts].T, ora["lse"], atol=2e-4 if w.dtype == "bf16" else 2e-5)
+    H.log(f"[{label}] attention on oracle selection: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_n1024", "prefill_n4096"])
+def test_prefill_full(name):
+    check_prefill(W.WORKLOADS[name], name)
+
+
+def test_prefill_ragged_multi_head():
+    w = W.WORKLOADS["prefill_n4096"].with_(name="ragged", batch=2, seq_len=4133, n_q_heads=32, n_kv_heads=2,
+                                           top_k=8, seed=11)
+    check_prefill(w, "ragged_b2_n4133_k8", sample=1500)
+
+
+@pytest.mark.parametrize("d,hq,hkv,K,n,dtype", [
+    (64, 8, 1, 6, 3000, "bf16"),      # d = 64, G = 8
+    (128, 2, 2, 5, 2000, "bf16"),     # G = 1
+    (128, 4, 2, 3, 1500, "bf16"),     # G = 2
+    (64, 16, 1, 2, 1100, "f32"),      # fp32, G = 16, small K
+    (128, 4, 1, 32, 2600, "bf16"),    # K = 32 > number of leaves / 2
+])
+def test_prefill_shapes(d, hq, hkv, K, n, dtype):
+    w = W.WORKLOADS["prefill_n4096"].with_(name="shape", head_dim=d, n_q_heads=hq, n_kv_heads=hkv, top_k=K,
+                                           seq_len=n, dtype=dtype, seed=20 + d + hq + K)
+    check_prefill(w, f"shape_d{d}_g{hq // hkv}_k{K}_n{n}_{dtype}")
+
+
+@pytest.mark.parametrize("n", [1, 50, 64, 65, 130, 257])
+def test_prefill_tiny_lengths(n):
+    w = W.WORKLOADS["prefill_n4096"].with_(name="short", seq_len=n, top_k=2, n_q_heads=4, seed=30 + n)
+    check_prefill(w, f"short_n{n}")
+
+
+def test_all_leaves_selected_is_dense_causal_attention():
+    w = W.WORKLOADS["prefill_n4096"].with_(name="dense", seq_len=700, top_k=12, seed=41)
+    q, k, v = W.prefill_inputs(w, bits=True)
+    g = H.run_gpu_prefill(w, q, k, v)
+    sel = g["sel"].cpu().numpy()[0, 0]
+    for t in range(700):
+        assert [x for x in sel[t] if x >= 0] == list(range(t // 64 + 1))
+    ts = np.arange(0, 700, 7)
+    want = oracle.dense_causal_attention(H.host_values(q[0]).astype(np.float64)[ts],
+                                         H.host_values(k[0, :, 0]).astype(np.float64),
+                                         H.host_values(v[0, :, 0]).astype(np.float64), ts)
+    ma, rl = H.attn_errors(g["o"].float().cpu().numpy()[0, ts], want)
+    assert ma <= 1e-2 and rl <= 5e-3, (ma, rl)
+
+
+def test_strided_inputs_match_contiguous():
+    """Q/K/V as views into one packed [B, N, Hq + 2 Hkv, d] buffer give identical results."""
+    w = W.WORKLOADS["prefill_n4096"].with_(name="strided", seq_len=2000, batch=2, n_q_heads=8, n_kv_heads=2,
+                                           top_k=4, seed=43)
+    q, k, v = W.prefill_inputs(w, bits=True)
+    ref = H.run_gpu_prefill(w, q, k, v)
+    packed = torch.cat([H.to_device(q, w), H.to_device(k, w), H.to_device(v, w)], dim=2)
+    qs, ks, vs = packed[:, :, :8], packed[:, :, 8:10], packed[:, :, 10:12]
+    assert not qs.is_contiguous()
+    pyr = binding.build_pyramid(ks)
+    sel = binding.select_blocks(qs, ks, pyr, 4)
+    o = binding.sparse_attn_fwd(qs, ks, vs, sel)
+    assert torch.equal(pyr, ref["pyr"]) and torch.equal(sel, ref["sel"]) and torch.equal(o, ref["o"])
+
+
+def test_repeat_runs_are_bit_identical():
+    w = W.WORKLOADS["prefill_n4096"]
+    q, k, v = W.prefill_inputs(w, bits=True)
+    a = H.run_gpu_prefill(w, q, k, v)
+    b = H.run_gpu_prefill(w, q, k, v)
+    for key in ("pyr", "sel", "sel_u", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name,sample", [("prefill_n32768", 300), ("prefill_n262144", 1200)])
+def test_prefill_full_size_sampled(name, sample):
+    check_prefill(W.WORKLOADS[name], name, sample=sample)
+
+
+# ----------------------------------------------------------------------------- decode
+def run_decode(w: W.Workload, batches, n0: int, steps: int, label: str, check_units=None):
+    B = len(batches)
+    G, K, d = w.group, w.top_k, w.head_dim
+    cap = n0 + steps
+    H.log(f"[{label}] decode inputs B={B} ctx={n0} steps={steps} Hq={w.n_q_heads} Hkv={w.n_kv_heads} K={K}")
+    ctx_w = w.with_(seq_len=n0)
+    _, k0, v0 = W.prefill_inputs(ctx_w, batches=batches, bits=True, with_q=False)
+    kc = torch.zeros((B, cap, w.n_kv_heads, d), dtype=H.torch_dtype(w), device=H.DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :n0] = H.to_device(k0, w)
+    vc[:, :n0] = H.to_device(v0, w)
+    pyr = binding.build_pyramid(kc, n=n0, capacity=cap)
+    toks = {name: np.stack([np.stack([W.decode_tokens(w, name, b, h) for h in range(nh)], axis=1)
+                            for b in batches]) for name, nh in (("q", w.n_q_heads), ("k", w.n_kv_heads),
+                                                                ("v", w.n_kv_heads))}
+    dq, dk, dv = (H.to_device(toks[x], w) for x in ("q", "k", "v"))        # [B, steps, H, d]
+    outs, sels = [], []
+    H.log(f"[{label}] GPU decode steps")
+    for s in range(steps):
+        o, sel = binding.decode_step(dq[:, s].contiguous(), dk[:, s].contiguous(), dv[:, s].contiguous(),
+                                     kc, vc, pyr, n0 + s, K)
+        outs.append(o.float().cpu().numpy())
+        sels.append(sel.cpu().numpy())
+    torch.cuda.synchronize()
+    # incremental pyramid == rebuild, bit for bit (valid nodes of the final length)
+    rebuilt = binding.build_pyramid(kc, n=cap, capacity=cap).cpu().numpy()
+    got = pyr.cpu().numpy()
+    for bi in range(B):
+        for kvh in range(w.n_kv_heads):
+            for a, r in zip(_pyramid_levels(got[bi, kvh], cap, cap), _pyramid_levels(rebuilt[bi, kvh], cap, cap)):
+                np.testing.assert_array_equal(a, r)
+    units = check_units if check_units is not None else [(bi, h) for bi in range(B) for h in range(w.n_kv_heads)]
+    n_bad = n_total = 0
+    worst = (0.0, 0.0)
+    tol_abs, tol_rel = H.attn_tolerance(w)
+    for bi, kvh in units:
+        H.log(f"[{label}] oracle decode unit b={batches[bi]} kvh={kvh}")
+        st = oracle.DecodeState(H.host_values(k0[bi, :, kvh]).astype(np.float64),
+                                H.host_values(v0[bi, :, kvh]).astype(np.float64), capacity=cap)
+        for s in range(steps):
+            qh = toks["q"][bi, s, kvh * G:(kvh + 1) * G].astype(np.float64)
+            osel, ogap, oo, _ = st.step(qh, toks["k"][bi, s, kvh], toks["v"][bi, s, kvh], K)
+            gsel = sels[s][bi, kvh]
+            n_total += 1
+            if not np.array_equal(gsel, osel):
+                assert ogap < H.GAP_LIMIT, (label, bi, kvh, s, gsel.tolist(), osel.tolist(), ogap)
+                n_bad += 1
+                continue
+            ma, rl = H.attn_errors(outs[s][bi, kvh * G:(kvh + 1) * G], oo)
+            worst = (max(worst[0], ma), max(worst[1], rl))
+            assert ma <= tol_abs and rl <= tol_rel, (label, bi, kvh, s, ma, rl)
+    H.assert_mismatch_budget(n_bad, n_total, label)
+    H.log(f"[{label}] decode attention max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+
+
+def test_decode_crosses_leaf_and_level_boundaries():
+    # 1000 keys = 16 leaves (a power of two): the first step adds leaf 16 and a new root level
+    w = W.WORKLOADS["decode_b64_ctx131072"].with_(name="dec_small", n_q_heads=8, n_kv_heads=2, top_k=4,
+                                                  decode_steps=130, seed=50)
+    run_decode(w, [0, 1], 1024 - 24, 130, "decode_small")
+
+
+def test_decode_fp32_and_wide_group():
+    w = W.WORKLOADS["tiny_f32_n1024"].with_(name="dec_f32", decode_steps=70, seed=51)
+    run_decode(w, [0], 200, 70, "decode_f32_g4")
+    w16 = W.WORKLOADS["decode_b64_ctx131072"].with_(name="dec_g16", n_q_heads=16, n_kv_heads=1, top_k=8,
+                                                    decode_steps=40, seed=52)
+    run_decode(w16, [0], 3000, 40, "decode_bf16_g16_k8")
+
+
+def test_decode_from_a_single_key():
+    w = W.WORKLOADS["decode_b64_ctx131072"].with_(name="dec_one", n_q_heads=4, n_kv_heads=1, top_k=2,
+                                                  decode_steps=140, seed=53)
+    run_decode(w, [0], 1, 140, "decode_from_one_key")
+
+
+def test_decode_full_context_subset():
+    """The 131072-token decode workload for sequences 0 and 1 (all 8 KV heads), all 256 steps."""
+    w = W.WORKLOADS["decode_b64_ctx131072"]
+    run_decode(w, [0, 1], w.seq_len, w.decode_steps, "decode_ctx131072_b0-1")
