@@ -123,7 +123,7 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     cfg = binding.make_cfg(B, N, Hq, w.n_kv_heads, d, K, q.dtype)
     ws = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
     sel = torch.empty((B, w.n_kv_heads, N, K), dtype=torch.int32, device=q.device)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)   # fp32 attention output
 
     def step(ev=None):
         if ev is not None:

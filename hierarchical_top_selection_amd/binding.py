@@ -53,10 +53,10 @@ _SIGNATURES = {
     "pisa_select_blocks": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
-                                            PisaTensor, ctypes.c_void_p, ctypes.c_void_p]),
+                                            PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "pisa_decode_step": (ctypes.c_int, [_P(PisaCfg), ctypes.c_int32, PisaTensor, PisaTensor, PisaTensor,
                                         PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p, PisaTensor,
-                                        ctypes.c_void_p]),
+                                        ctypes.c_int, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -171,25 +171,29 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: in
 
 
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, scale: float = 0.0,
-                    out: torch.Tensor | None = None, return_lse: bool = False):
-    """Attention over the selected blocks: o [B, N, Hq, d] (and row LSE [B, Hq, N] if asked)."""
+                    out: torch.Tensor | None = None, return_lse: bool = False, out_dtype: torch.dtype | None = None):
+    """Attention over the selected blocks: o [B, N, Hq, d] (and row LSE [B, Hq, N] if asked).
+
+    The output is float32 or bfloat16 (default: q's dtype, or the dtype of ``out``).
+    """
     B, N, Hq, d = q.shape
     top_k = sel.shape[-1]
     cfg = _cfg_from(q, k, top_k, scale)
     if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, k.shape[2], N, top_k):
         raise ValueError("selection must be a contiguous int32 [B, Hkv, N, K] tensor")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
     _check("pisa_sparse_attn_fwd", lib().pisa_sparse_attn_fwd(
         ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()),
-        _tensor(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+        _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
     return (out, lse) if return_lse else out
 
 
 def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                 v_cache: torch.Tensor, pyr: torch.Tensor, n_ctx: int, top_k: int, scale: float = 0.0,
-                out: torch.Tensor | None = None, sel_out: torch.Tensor | None = None):
+                out: torch.Tensor | None = None, sel_out: torch.Tensor | None = None,
+                out_dtype: torch.dtype | None = None):
     """One decode step for every sequence: q [B, Hq, d], k_new/v_new [B, Hkv, d], caches [B, cap, Hkv, d].
 
     Appends at position n_ctx, updates the pyramid in place and returns (o [B, Hq, d], sel [B, Hkv, K]).
@@ -199,13 +203,13 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cac
     cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, k_cache.dtype, scale)
     _dtype_code(k_cache)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if sel_out is None:
         sel_out = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
     _check("pisa_decode_step", lib().pisa_decode_step(
         ctypes.byref(cfg), n_ctx, _tensor(q, False), _tensor(k_new, False), _tensor(v_new, False),
         _tensor(k_cache), _tensor(v_cache), ctypes.c_void_p(pyr.data_ptr()), ctypes.c_void_p(sel_out.data_ptr()),
-        _tensor(out, False), _stream(q)))
+        _tensor(out, False), _dtype_code(out), _stream(q)))
     return out, sel_out
 
 

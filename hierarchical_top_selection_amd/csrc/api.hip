@@ -198,9 +198,11 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
 }
 
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor_mut o, float* row_lse, void* stream) {
+                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 void* stream) {
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
+  if (o_dtype != PISA_F32 && o_dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
   if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
   if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
   if ((st = check_tensor(v.ptr, v.stride_b, v.stride_t, v.stride_h)) != PISA_OK) return st;
@@ -215,15 +217,16 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.row_lse = row_lse;
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
-  a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = o_dtype == PISA_BF16;
   return hip_status(pisa::launch_attention(a, (hipStream_t)stream));
 }
 
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
                              pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache, float* pyr,
-                             int32_t* sel_out, pisa_tensor_mut o, void* stream) {
+                             int32_t* sel_out, pisa_tensor_mut o, pisa_dtype o_dtype, void* stream) {
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
+  if (o_dtype != PISA_F32 && o_dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
   const int G = cfg->n_q_heads / cfg->n_kv_heads;
   if (n_ctx < 0 || n_ctx + 1 > cfg->seq_len) return PISA_ERR_INVALID_ARG;
   if (G * 2 * cfg->top_k > 256) return PISA_ERR_UNSUPPORTED;
@@ -244,6 +247,7 @@ pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, 
   a.o = o.ptr; a.o_sb = o.stride_b; a.o_sh = o.stride_h;
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = G; a.head_dim = cfg->head_dim;
   a.top_k = cfg->top_k; a.n_ctx = n_ctx; a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  a.out_bf16 = o_dtype == PISA_BF16;
   a.lv = make_levels(n_ctx + 1, cfg->seq_len);
   return hip_status(pisa::launch_decode(a, (hipStream_t)stream));
 }

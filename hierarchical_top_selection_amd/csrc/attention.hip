@@ -17,7 +17,7 @@
 
 namespace pisa {
 
-template <typename T, int D>
+template <typename T, typename TO, int D>
 __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
   constexpr bool kBF = std::is_same<T, __bf16>::value;
@@ -134,11 +134,11 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
 
   if (col < a.group) {
     const float inv = 1.f / l_run;
-    T* orow = reinterpret_cast<T*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh;
+    TO* orow = reinterpret_cast<TO*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<T>(o[dt][i] * inv);
+      for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<TO>(o[dt][i] * inv);
     if (a.row_lse && g == 0) {
       const int hq = a.n_kv_heads * a.group;
       a.row_lse[((int64_t)b * hq + head) * a.n + t] = m_run + logf(l_run);
@@ -146,16 +146,21 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int D>
+template <typename T, typename TO, int D>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
-  hipLaunchKernelGGL((attention_kernel<T, D>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attention_kernel<T, TO, D>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+template <typename T, typename TO>
+hipError_t launch_attention_o(const AttnArgs& a, hipStream_t s) {
+  return a.head_dim == 64 ? launch_attention_t<T, TO, 64>(a, s) : launch_attention_t<T, TO, 128>(a, s);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.bf16) return a.head_dim == 64 ? launch_attention_t<__bf16, 64>(a, s) : launch_attention_t<__bf16, 128>(a, s);
-  return a.head_dim == 64 ? launch_attention_t<float, 64>(a, s) : launch_attention_t<float, 128>(a, s);
+  if (a.bf16) return a.out_bf16 ? launch_attention_o<__bf16, __bf16>(a, s) : launch_attention_o<__bf16, float>(a, s);
+  return a.out_bf16 ? launch_attention_o<float, __bf16>(a, s) : launch_attention_o<float, float>(a, s);
 }
 
 }  // namespace pisa

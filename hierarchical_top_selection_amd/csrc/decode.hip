@@ -62,7 +62,7 @@ struct DecodeLds {
   }
 };
 
-template <typename T, int D, int G>
+template <typename T, typename TO, int D, int G>
 __global__ __launch_bounds__(256) void decode_fused_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) float smem[];
   const int width = 2 * a.top_k, K = a.top_k;
@@ -285,12 +285,12 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < kCols; ++c) part[(wave * G + h) * D + lane * kCols + c] = accv[h][c];
   __syncthreads();
-  T* obase = reinterpret_cast<T*>(a.o) + b * a.o_sb + (int64_t)kvh * G * a.o_sh;
+  TO* obase = reinterpret_cast<TO*>(a.o) + b * a.o_sb + (int64_t)kvh * G * a.o_sh;
   for (int e = tid; e < G * D; e += blockDim.x) {
     const int h = e / D, c = e % D;
     const float v = ((part[(0 * G + h) * D + c] + part[(1 * G + h) * D + c]) + part[(2 * G + h) * D + c]) +
                     part[(3 * G + h) * D + c];
-    obase[h * a.o_sh + c] = from_f32<T>(v);
+    obase[h * a.o_sh + c] = from_f32<TO>(v);
   }
   if (a.sel_out && tid < K) a.sel_out[(int64_t)bh * K + tid] = tid < nsel ? selv[tid] : -1;
 }
@@ -302,7 +302,7 @@ size_t decode_lds_bytes(int group, int width, int head_dim) {
 template <typename T, int D, int G>
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) {
   const size_t lds = decode_lds_bytes(G, 2 * a.top_k, D);
-  auto kern = decode_fused_kernel<T, D, G>;
+  auto kern = a.out_bf16 ? decode_fused_kernel<T, __bf16, D, G> : decode_fused_kernel<T, float, D, G>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -71,7 +71,8 @@ struct AttnArgs {
   float* row_lse;        // optional [B][Hq][N]
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
-  bool bf16;
+  bool bf16;             // element type of q, k, v
+  bool out_bf16;         // element type of o
 };
 
 struct DecodeArgs {
@@ -91,7 +92,8 @@ struct DecodeArgs {
   int64_t o_sb, o_sh;
   int batch, n_kv_heads, group, head_dim, top_k, n_ctx;
   float scale;
-  bool bf16;
+  bool bf16;                // element type of q, k/v (new and cached)
+  bool out_bf16;            // element type of o
   Levels lv;                // sizes for length n_ctx + 1, capacity offsets
 };
 

@@ -146,12 +146,14 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
  *   sel     : int32 [B][H_kv][N][K] (any entry < 0 ends nothing: it is skipped;
  *             valid entries must satisfy 64 * j <= t, else the result for that
  *             token is unspecified)
- *   o       : [B][N][H_q][d] output, cfg->dtype
+ *   o       : [B][N][H_q][d] output of element type o_dtype (float32 keeps the
+ *             fp32 accumulator; bfloat16 rounds it to nearest-even)
  *   row_lse : optional float32 [B][H_q][N] output (NULL to skip): natural-log
  *             normaliser of each row's softmax
  */
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor_mut o, float* row_lse, void* stream);
+                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 void* stream);
 
 /*
  * decode_step - one autoregressive step for every sequence (Method steps,
@@ -167,12 +169,13 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
  *   k_cache, v_cache  : [B][capacity][H_kv][d], updated in place
  *   pyr               : pyramid of the cache (capacity layout), updated in place
  *   sel_out           : optional int32 [B][H_kv][K] (NULL to skip)
- *   o                 : [B][H_q][d] output (stride_t ignored)
+ *   o                 : [B][H_q][d] output of element type o_dtype (stride_t ignored)
  * Requires G * 2K <= 256 (leaf logits are staged on chip).
  */
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
                              pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache,
-                             float* pyr, int32_t* sel_out, pisa_tensor_mut o, void* stream);
+                             float* pyr, int32_t* sel_out, pisa_tensor_mut o, pisa_dtype o_dtype,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,9 +63,11 @@ def run_gpu_prefill(w: W.Workload, q: np.ndarray, k: np.ndarray, v: np.ndarray, 
     qd, kd, vd = to_device(q, w), to_device(k, w), to_device(v, w)
     pyr = binding.build_pyramid(kd)
     sel, sel_u = binding.select_blocks(qd, kd, pyr, K, return_scores=True)
-    o, lse = binding.sparse_attn_fwd(qd, kd, vd, sel, return_lse=True)
+    o, lse = binding.sparse_attn_fwd(qd, kd, vd, sel, return_lse=True, out_dtype=torch.float32)
+    o_native = binding.sparse_attn_fwd(qd, kd, vd, sel)          # output in the input dtype
     torch.cuda.synchronize()
-    return {"q": qd, "k": kd, "v": vd, "pyr": pyr, "sel": sel, "sel_u": sel_u, "o": o, "lse": lse}
+    return {"q": qd, "k": kd, "v": vd, "pyr": pyr, "sel": sel, "sel_u": sel_u, "o": o, "lse": lse,
+            "o_native": o_native}
 
 
 def oracle_prefill(w: W.Workload, q, k, v, b: int, kvh: int, ts: np.ndarray, top_k: int | None = None):
@@ -102,4 +104,15 @@ def attn_errors(got: np.ndarray, want: np.ndarray):
 
 
 def attn_tolerance(w: W.Workload):
+    """(max-abs, relative L2) gates for float32 outputs."""
     return (1e-4, 1e-5) if w.dtype == "f32" else (1e-2, 5e-3)
+
+
+def assert_bf16_output(got: np.ndarray, want: np.ndarray, label: str) -> None:
+    """bfloat16 outputs: the fp32 gates plus half a bf16 ulp of the exact value (<= |x| / 256)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want) - np.abs(want) / 256.0
+    assert err.size == 0 or err.max() <= 1e-2, (label, "bf16 output", float(err.max()))
+    _, rl = attn_errors(got, want)
+    assert rl <= 5e-3, (label, "bf16 output rel-L2", rl)

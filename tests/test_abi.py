@@ -81,7 +81,10 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
     # decode: position beyond capacity, and the on-chip limit G * 2K <= 256
     o = binding.PisaTensor(4096, 0, 0, 128)
     assert lib.pisa_decode_step(ctypes.byref(cfg), 4096, good, good, good, good, good, ctypes.c_void_p(4096),
-                                None, o, None) == 1
+                                None, o, 1, None) == 1
     big = _cfg(top_k=16, n_q_heads=16)
     assert lib.pisa_decode_step(ctypes.byref(big), 10, good, good, good, good, good, ctypes.c_void_p(4096),
-                                None, o, None) == 2
+                                None, o, 1, None) == 2
+    # output element type must be float32 or bfloat16
+    assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 5,
+                                    None, None) == 1

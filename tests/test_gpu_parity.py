@@ -34,7 +34,8 @@ def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: in
     pyr = g["pyr"].cpu().numpy()
     sel = g["sel"].cpu().numpy()
     sel_u = g["sel_u"].cpu().numpy()
-    o = g["o"].float().cpu().numpy()
+    o = g["o"].cpu().numpy()
+    o_native = g["o_native"].float().cpu().numpy()
     sel_in = g["sel"].clone()
     n_bad = n_total = 0
     units = []
@@ -67,13 +68,15 @@ def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: in
             tol_abs, tol_rel = H.attn_tolerance(w)
             ma, rl = H.attn_errors(o[b, ts][:, heads][agree], ora["o"][agree])
             assert ma <= tol_abs and rl <= tol_rel, (label, "end-to-end", ma, rl)
+            if w.dtype == "bf16":
+                H.assert_bf16_output(o_native[b, ts][:, heads][agree], ora["o"][agree], label)
             sel_in[b, kvh, torch.from_numpy(ts).to(H.DEV)] = torch.from_numpy(ora["sel"].astype(np.int32)).to(H.DEV)
             units.append((b, kvh, ts, ora))
     H.assert_mismatch_budget(n_bad, n_total, label)
     H.log(f"[{label}] max |du| on selected leaves {max_du:.3g}")
     # attention on the oracle's own selection (fed to the kernel as input)
-    o2, lse2 = binding.sparse_attn_fwd(g["q"], g["k"], g["v"], sel_in, return_lse=True)
-    o2 = o2.float().cpu().numpy()
+    o2, lse2 = binding.sparse_attn_fwd(g["q"], g["k"], g["v"], sel_in, return_lse=True, out_dtype=torch.float32)
+    o2 = o2.cpu().numpy()
     lse2 = lse2.cpu().numpy()
     worst = (0.0, 0.0)
     for b, kvh, ts, ora in units:
@@ -128,7 +131,7 @@ def test_all_leaves_selected_is_dense_causal_attention():
     want = oracle.dense_causal_attention(H.host_values(q[0]).astype(np.float64)[ts],
                                          H.host_values(k[0, :, 0]).astype(np.float64),
                                          H.host_values(v[0, :, 0]).astype(np.float64), ts)
-    ma, rl = H.attn_errors(g["o"].float().cpu().numpy()[0, ts], want)
+    ma, rl = H.attn_errors(g["o"].cpu().numpy()[0, ts], want)
     assert ma <= 1e-2 and rl <= 5e-3, (ma, rl)
 
 
@@ -144,7 +147,7 @@ def test_strided_inputs_match_contiguous():
     pyr = binding.build_pyramid(ks)
     sel = binding.select_blocks(qs, ks, pyr, 4)
     o = binding.sparse_attn_fwd(qs, ks, vs, sel)
-    assert torch.equal(pyr, ref["pyr"]) and torch.equal(sel, ref["sel"]) and torch.equal(o, ref["o"])
+    assert torch.equal(pyr, ref["pyr"]) and torch.equal(sel, ref["sel"]) and torch.equal(o, ref["o_native"])
 
 
 def test_repeat_runs_are_bit_identical():
@@ -152,7 +155,7 @@ def test_repeat_runs_are_bit_identical():
     q, k, v = W.prefill_inputs(w, bits=True)
     a = H.run_gpu_prefill(w, q, k, v)
     b = H.run_gpu_prefill(w, q, k, v)
-    for key in ("pyr", "sel", "sel_u", "o", "lse"):
+    for key in ("pyr", "sel", "sel_u", "o", "lse", "o_native"):
         assert torch.equal(a[key], b[key]), key
 
 
@@ -182,8 +185,8 @@ def run_decode(w: W.Workload, batches, n0: int, steps: int, label: str, check_un
     H.log(f"[{label}] GPU decode steps")
     for s in range(steps):
         o, sel = binding.decode_step(dq[:, s].contiguous(), dk[:, s].contiguous(), dv[:, s].contiguous(),
-                                     kc, vc, pyr, n0 + s, K)
-        outs.append(o.float().cpu().numpy())
+                                     kc, vc, pyr, n0 + s, K, out_dtype=torch.float32)
+        outs.append(o.cpu().numpy())
         sels.append(sel.cpu().numpy())
     torch.cuda.synchronize()
     # incremental pyramid == rebuild, bit for bit (valid nodes of the final length)
