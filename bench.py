@@ -122,6 +122,7 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     pyr = torch.empty((B, w.n_kv_heads, binding.pyramid_nodes(N), d), dtype=torch.float32, device=q.device)
     cfg = binding.make_cfg(B, N, Hq, w.n_kv_heads, d, K, q.dtype)
     ws = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    ws_attn = torch.empty(max(1, binding.attn_workspace_bytes(cfg)), dtype=torch.uint8, device=q.device)
     sel = torch.empty((B, w.n_kv_heads, N, K), dtype=torch.int32, device=q.device)
     o = torch.empty(q.shape, dtype=torch.float32, device=q.device)   # fp32 attention output
 
@@ -134,7 +135,7 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
         binding.select_blocks(q, k, pyr, K, workspace=ws, out=sel)
         if ev is not None:
             ev[2].record()
-        binding.sparse_attn_fwd(q, k, v, sel, out=o)
+        binding.sparse_attn_fwd(q, k, v, sel, out=o, workspace=ws_attn)
         if ev is not None:
             ev[3].record()
 
@@ -164,12 +165,24 @@ def main() -> int:
     ap.add_argument("--also", default="prefill_n32768", help="comma-separated extra workloads to report")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (3 times), for scaling HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this path runs on one GPU; runs on more than one GPU are not supported "
               "(the design notes describe how it would shard)", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        import torch
+
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "reads": src.numel() * 4, "writes": src.numel() * 4}))
+        return 0
     w = W.WORKLOADS[args.workload]
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)   # before any GPU use
 

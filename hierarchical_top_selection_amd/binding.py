@@ -52,8 +52,10 @@ _SIGNATURES = {
     "pisa_select_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
     "pisa_select_blocks": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pisa_attn_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
     "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
-                                            PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+                                            PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
     "pisa_decode_step": (ctypes.c_int, [_P(PisaCfg), ctypes.c_int32, PisaTensor, PisaTensor, PisaTensor,
                                         PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p, PisaTensor,
                                         ctypes.c_int, ctypes.c_void_p]),
@@ -170,8 +172,13 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: in
     return (out, scores) if return_scores else out
 
 
+def attn_workspace_bytes(cfg: PisaCfg) -> int:
+    return int(lib().pisa_attn_workspace_bytes(ctypes.byref(cfg)))
+
+
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, scale: float = 0.0,
-                    out: torch.Tensor | None = None, return_lse: bool = False, out_dtype: torch.dtype | None = None):
+                    out: torch.Tensor | None = None, return_lse: bool = False, out_dtype: torch.dtype | None = None,
+                    workspace: torch.Tensor | None = None):
     """Attention over the selected blocks: o [B, N, Hq, d] (and row LSE [B, Hq, N] if asked).
 
     The output is float32 or bfloat16 (default: q's dtype, or the dtype of ``out``).
@@ -184,9 +191,14 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
+    need = attn_workspace_bytes(cfg)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if need else (0, 0)
     _check("pisa_sparse_attn_fwd", lib().pisa_sparse_attn_fwd(
         ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()),
-        _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+        _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+        ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_len), _stream(q)))
     return (out, lse) if return_lse else out
 
 

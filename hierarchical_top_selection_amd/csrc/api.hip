@@ -79,8 +79,8 @@ pisa_status hip_status(hipError_t e) {
 }
 
 struct SelectWorkspace {
-  size_t cand, leaf_u, pairs, leaf_off, total;
-  int n_windows;
+  size_t cand, leaf_u, pairs, leaf_off, items, n_items, total;
+  int n_windows, item_cap;
 };
 
 SelectWorkspace select_layout(const pisa_cfg* c) {
@@ -93,7 +93,13 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   w.leaf_u = align256(w.cand + slots * 4);
   w.pairs = align256(w.leaf_u + slots * 4);
   w.leaf_off = align256(w.pairs + slots * 4);
-  w.total = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
+  // items per window: sum over leaves of ceil(count / P) <= window pairs / P + distinct leaves
+  const int64_t window_pairs = (int64_t)kWindow * 2 * c->top_k;
+  w.item_cap = (int)((window_pairs + pisa::kPairsPerItem - 1) / pisa::kPairsPerItem +
+                     (m1 < window_pairs ? m1 : window_pairs));
+  w.items = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
+  w.n_items = align256(w.items + (size_t)bh * w.n_windows * w.item_cap * 4);
+  w.total = align256(w.n_items + (size_t)bh * w.n_windows * 4);
   return w;
 }
 
@@ -162,6 +168,8 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   float* leaf_u = reinterpret_cast<float*>(base + w.leaf_u);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + w.pairs);
   int32_t* leaf_off = reinterpret_cast<int32_t*>(base + w.leaf_off);
+  int32_t* items = reinterpret_cast<int32_t*>(base + w.items);
+  int32_t* n_items = reinterpret_cast<int32_t*>(base + w.n_items);
   const int N = cfg->seq_len, G = cfg->n_q_heads / cfg->n_kv_heads, width = 2 * cfg->top_k;
   const int m1 = (N + pisa::kLeaf - 1) / pisa::kLeaf;
   const bool bf16 = cfg->dtype == PISA_BF16;
@@ -180,6 +188,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   c.cand = cand; c.pairs = pairs; c.leaf_off = leaf_off;
   c.batch = cfg->batch; c.n_kv_heads = cfg->n_kv_heads; c.n = N; c.width = width;
   c.n_leaves = m1; c.window = kWindow; c.n_windows = w.n_windows;
+  c.items = items; c.n_items = n_items; c.item_cap = w.item_cap;
   if ((st = hip_status(pisa::launch_cluster(c, s))) != PISA_OK) return st;
 
   pisa::LeafArgs l;
@@ -188,6 +197,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   l.pairs = pairs; l.leaf_off = leaf_off; l.leaf_u = leaf_u;
   l.batch = cfg->batch; l.n_kv_heads = cfg->n_kv_heads; l.group = G; l.head_dim = cfg->head_dim;
   l.n = N; l.width = width; l.n_leaves = m1; l.window = kWindow; l.n_windows = w.n_windows;
+  l.items = items; l.n_items = n_items; l.item_cap = w.item_cap;
   l.scale = scale; l.bf16 = bf16;
   if ((st = hip_status(pisa::launch_leaf_lse(l, s))) != PISA_OK) return st;
 
@@ -197,11 +207,20 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   return hip_status(pisa::launch_topk(t, s));
 }
 
+size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg) {
+  if (check_cfg(cfg) != PISA_OK) return 0;
+  if (cfg->dtype != PISA_BF16) return 0;
+  const int64_t m1 = (cfg->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
+  return align256((size_t)cfg->batch * cfg->n_kv_heads * m1 * pisa::kLeaf * cfg->head_dim * 2);
+}
+
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
-                                 void* stream) {
+                                 void* ws, size_t ws_bytes, void* stream) {
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
+  const size_t need = pisa_attn_workspace_bytes(cfg);
+  if (need && (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))) return PISA_ERR_WORKSPACE;
   if (o_dtype != PISA_F32 && o_dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
   if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
   if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
@@ -215,6 +234,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.sel = sel;
   a.o = o.ptr; a.o_sb = o.stride_b; a.o_st = o.stride_t; a.o_sh = o.stride_h;
   a.row_lse = row_lse;
+  a.vt = static_cast<__bf16*>(ws);
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
   a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = o_dtype == PISA_BF16;

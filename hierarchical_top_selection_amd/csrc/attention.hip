@@ -4,28 +4,255 @@
 //
 // One wave per (b, kvh, token): the group's G <= 16 query heads are the 16
 // columns of every MFMA.  Per selected block the wave forms S^T = K_j Q^T
-// (keys on rows, heads on columns, K rows streamed from HBM straight into A
-// fragments), updates an online softmax per head column, and accumulates
-// O^T += V_j^T P^T.  Keeping S transposed makes P^T's B fragment exactly the
-// lane's own accumulator values; only V has to be read transposed, which the
-// wave does from a private, bank-padded LDS stage (32 keys at a time for bf16,
-// 16 for fp32).  bf16 inputs run on v_mfma_f32_16x16x32_bf16 with P rounded to
-// bf16 for the PV product; fp32 inputs on v_mfma_f32_16x16x4_f32.
-#include <type_traits>
-
+// (keys on rows, heads on columns, K rows loaded straight into A fragments),
+// updates an online softmax per head column (base-2 exponentials on pre-scaled
+// logits), and accumulates O^T += V_j^T P^T.  Keeping S transposed makes P^T's
+// B fragment exactly the lane's own accumulator values.
+//
+// The kernel is bound by gathering K/V blocks from memory.  The bf16 path first
+// writes V transposed per leaf block (one cheap pass over V), loads the K rows
+// of each block in a permuted key order, and thereby gets both PV operands as
+// plain 16-byte loads straight into MFMA fragments -- no LDS at all.  It is
+// software-pipelined one block ahead: as soon as the S^T MFMAs have consumed
+// K_j (and the PV MFMAs V_j), the registers are refilled for block j+1, so the
+// gather latency overlaps the softmax and MFMA work.  fp32 inputs take a plain
+// path that stages V through LDS, on v_mfma_f32_16x16x4_f32.
 #include "kernels.h"
 
 namespace pisa {
 
-template <typename T, typename TO, int D>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
-  typedef typename RawFrag<T, D>::type Frag;
-  constexpr bool kBF = std::is_same<T, __bf16>::value;
-  constexpr int kChunk = kBF ? 32 : 16;     // keys staged per LDS round
-  constexpr int kPad = kBF ? 8 : 4;         // row padding (elements): conflict-free transposed reads
-  constexpr int kVec = 16 / sizeof(T);      // elements per 16-byte load
-  constexpr int kRowVecs = D / kVec;
-  __shared__ __align__(16) T vstage[4][kChunk][D + kPad];
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename TO>
+__device__ inline void store4(TO* p, float a, float b, float c, float d);
+template <>
+__device__ inline void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ inline void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
+// Online-softmax update of one 64-key block held as acc[mt][r] (key 16 mt + 4 g + r,
+// head column of this lane): replaces acc by P (fp32) and returns the rescale factor
+// of the running output.  m_run is kept in base-2 units of the scaled logits.
+__device__ inline float softmax_block(floatx4 (&acc)[4], float c2, bool mask, int64_t first, int g, int64_t t,
+                                      int n, float& m_run, float& l_run) {
+  if (mask) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = first + 16 * mt + 4 * g + r;
+        if (key > t || key >= n) acc[mt][r] = kNegInf;
+      }
+  }
+  float tmax = kNegInf;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[mt][r]);
+  tmax = wave_max_xor(tmax, 16);
+  tmax = wave_max_xor(tmax, 32);
+  const float m_new = fmaxf(m_run, tmax * c2);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = exp2f(m_run - m_use);
+  float psum = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = exp2f(fmaf(acc[mt][r], c2, -m_use));
+      acc[mt][r] = p;
+      psum += p;
+    }
+  psum = wave_add_xor(psum, 16);
+  psum = wave_add_xor(psum, 32);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  return alpha;
+}
+
+template <typename TO>
+__device__ inline void finish_row(const AttnArgs& a, const floatx4* o, int nd16, float m_run, float l_run, int b,
+                                  int64_t t, int head, int g) {
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  TO* orow = reinterpret_cast<TO*>(a.o) + b * a.o_sb + t * a.o_st + (int64_t)head * a.o_sh;
+  for (int dt = 0; dt < nd16; ++dt)
+    store4<TO>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+  if (a.row_lse && g == 0) {
+    const int hq = a.n_kv_heads * a.group;
+    a.row_lse[((int64_t)b * hq + head) * a.n + t] = (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- bf16, pipelined
+// V^T blocks: vt[bh][leaf][c][64 keys] (keys past n are zero), so an 8-key run of one
+// value column is one 16-byte load.
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(AttnArgs a) {
+  __shared__ __bf16 tile[kLeaf][D + 8];
+  const int leaf = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh;
+  const int64_t first = (int64_t)leaf * kLeaf;
+  for (int e = threadIdx.x; e < kLeaf * D / 8; e += blockDim.x) {
+    const int r = e / (D / 8), cv = e % (D / 8);
+    const int64_t key = first + r;
+    const uint4 val = key < a.n ? *reinterpret_cast<const uint4*>(vbase + key * a.v_st + cv * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&tile[r][cv * 8]) = val;
+  }
+  __syncthreads();
+  const int m1 = ceil_div(a.n, kLeaf);
+  __bf16* dst = a.vt + (((int64_t)bh * m1 + leaf) * D) * kLeaf;
+  for (int e = threadIdx.x; e < D * kLeaf / 8; e += blockDim.x) {
+    const int c = e / (kLeaf / 8), k8 = e % (kLeaf / 8);
+    bf16x8 out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = tile[8 * k8 + i][c];
+    *reinterpret_cast<bf16x8*>(dst + (int64_t)c * kLeaf + 8 * k8) = out;
+  }
+}
+
+// Key order inside a block: M-tile mt = 2 kb + h, row m holds key 32 kb + 8 (m / 4) + 4 h + m % 4,
+// so in the S^T result lane group g of tiles (2 kb, 2 kb + 1) owns keys 32 kb + 8 g + 0..7 -- exactly
+// the k-slice that the lane supplies for the P V product of key half kb.
+__device__ inline int perm_key(int mt, int m) { return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3); }
+
+template <typename TO, int D>
+__global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
+  typedef FragBF16<D> Frag;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n) return;
+  const int bh = blockIdx.y;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int g = lane >> 4, col = lane & 15;
+  const int m1 = ceil_div(a.n, kLeaf);
+
+  const int head = kvh * a.group + col;
+  Frag qf;
+  if (col < a.group)
+    qf.load(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st + (int64_t)head * a.q_sh, g);
+  else
+    qf.zero();
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const __bf16* vtbase = a.vt + (int64_t)bh * m1 * D * kLeaf;
+  const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
+  const uint64_t valid = __ballot(my_sel >= 0);        // entries < 0 are skipped
+  const int nsel = __popcll(valid);
+  const float c2 = a.scale * kLog2e;
+
+  Frag kf[4];                 // A fragments of S^T = K Q^T, rows in perm_key order
+  bf16x8 vf[2][D / 16];       // A fragments of O^T = V^T P^T: [key half][value column tile]
+  // rows past the end of the sequence are clamped to the last key: their logits are masked
+  auto load_k = [&](int leaf) {
+    const int64_t first = (int64_t)leaf * kLeaf;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t key = min(first + perm_key(mt, col), (int64_t)a.n - 1);
+      kf[mt].load(kbase + key * a.k_st, g);
+    }
+  };
+  auto load_v = [&](int leaf) {
+    const __bf16* blk = vtbase + (int64_t)leaf * D * kLeaf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        vf[kb][dt] = *reinterpret_cast<const bf16x8*>(blk + (16 * dt + col) * kLeaf + 32 * kb + 8 * g);
+  };
+
+  floatx4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  uint64_t rest = valid;
+  int leaf = 0;
+  if (rest) {
+    leaf = __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64));
+    rest &= rest - 1;
+    load_k(leaf);
+    load_v(leaf);
+  }
+  for (int done = 0; done < nsel; ++done) {
+    const bool more = rest != 0;
+    const int leaf_n = more ? __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64)) : 0;
+    rest &= rest - 1;
+    const int64_t first = (int64_t)leaf * kLeaf;
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc[mt] = mma(kf[mt], qf, acc[mt]);
+    }
+    if (more) load_k(leaf_n);                          // K of the next block into the freed fragments
+
+    // acc[mt][r]: key first + perm_key(mt, 4 g + r) against head column col
+    if (first + kLeaf - 1 > t || first + kLeaf > a.n) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t key = first + perm_key(mt, 4 * g + r);
+          if (key > t || key >= a.n) acc[mt][r] = kNegInf;
+        }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[mt][r]);
+    tmax = wave_max_xor(tmax, 16);
+    tmax = wave_max_xor(tmax, 32);
+    const float m_new = fmaxf(m_run, tmax * c2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // arguments <= 0: no range fix-up needed
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -m_use));
+        psum += p;
+        pb[mt >> 1][4 * (mt & 1) + r] = (__bf16)p;      // k-index 4 h + r of key half kb = mt / 2
+      }
+    psum = wave_add_xor(psum, 16);
+    psum = wave_add_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      o[dt] *= alpha;
+      o[dt] = mfma_bf16(vf[0][dt], pb[0], o[dt]);
+      o[dt] = mfma_bf16(vf[1][dt], pb[1], o[dt]);
+    }
+    if (more) load_v(leaf_n);                          // V^T of the next block into the freed fragments
+    leaf = leaf_n;
+  }
+  if (col < a.group) finish_row<TO>(a, o, D / 16, m_run, l_run, b, t, head, g);
+}
+
+// ----------------------------------------------------------------------------- fp32, plain
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
+  typedef FragF32<D> Frag;
+  constexpr int kChunk = 16;                    // keys staged per LDS round (one key tile)
+  constexpr int kPad = 4;
+  constexpr int kRowVecs = D / 4;
+  __shared__ __align__(16) float vstage[4][kChunk][D + kPad];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -33,15 +260,18 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   const int bh = blockIdx.y;
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int g = lane >> 4, col = lane & 15;
-  T (*vs)[D + kPad] = vstage[wave];
+  float (*vs)[D + kPad] = vstage[wave];
 
   const int head = kvh * a.group + col;
   Frag qf;
-  if (col < a.group) qf.load(reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st + (int64_t)head * a.q_sh, g);
-  else qf.zero();
-  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.k_sb + kvh * a.k_sh;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.v_sb + kvh * a.v_sh;
+  if (col < a.group)
+    qf.load(reinterpret_cast<const float*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st + (int64_t)head * a.q_sh, g);
+  else
+    qf.zero();
+  const float* kbase = reinterpret_cast<const float*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + b * a.v_sb + kvh * a.v_sh;
   const int32_t* sel = a.sel + ((int64_t)bh * a.n + t) * a.top_k;
+  const float c2 = a.scale * kLog2e;
 
   floatx4 o[D / 16];
 #pragma unroll
@@ -61,106 +291,53 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
       acc[mt] = mma(kf, qf, acc[mt]);
     }
-    // acc[mt][i]: key first + 16 mt + 4 g + i against head column col
-    float tile_max = kNegInf;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = first + 16 * mt + 4 * g + i;
-        const float z = (key <= t && key < a.n) ? acc[mt][i] * a.scale : kNegInf;
-        acc[mt][i] = z;
-        tile_max = fmaxf(tile_max, z);
-      }
-    tile_max = wave_max_xor(tile_max, 16);
-    tile_max = wave_max_xor(tile_max, 32);
-    if (tile_max == kNegInf) continue;   // block holds no key <= t (masking is per key, so wave-uniform)
-    const float m_new = fmaxf(m_run, tile_max);
-    const float alpha = expf(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = expf(acc[mt][i] - m_new);
-        acc[mt][i] = p;
-        psum += p;
-      }
-    psum = wave_add_xor(psum, 16);
-    psum = wave_add_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    const bool mask = first + kLeaf - 1 > t || first + kLeaf > a.n;
+    const float alpha = softmax_block(acc, c2, mask, first, g, t, a.n, m_run, l_run);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-
 #pragma unroll
     for (int ch = 0; ch < kLeaf / kChunk; ++ch) {
       for (int e = lane; e < kChunk * kRowVecs; e += 64) {
         const int r = e / kRowVecs, cv = e % kRowVecs;
         const int64_t key = first + ch * kChunk + r;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (key < a.n) val = *reinterpret_cast<const uint4*>(vbase + key * a.v_st + cv * kVec);
-        *reinterpret_cast<uint4*>(&vs[r][cv * kVec]) = val;
+        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (key < a.n) val = *reinterpret_cast<const float4*>(vbase + key * a.v_st + cv * 4);
+        *reinterpret_cast<float4*>(&vs[r][cv * 4]) = val;
       }
       wave_lds_sync();
-      if constexpr (kBF) {
-        // k-index j of lane group g: keys 4g+j (j < 4) and 16+4g+j-4 (j >= 4) of this chunk
-        bf16x8 pb;
+      // chunk = key tile ch; k-step r: lane group g supplies key 4g + r
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = (__bf16)acc[2 * ch][i];
-          pb[4 + i] = (__bf16)acc[2 * ch + 1][i];
-        }
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          bf16x8 av;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            av[i] = vs[4 * g + i][16 * dt + col];
-            av[4 + i] = vs[16 + 4 * g + i][16 * dt + col];
-          }
-          o[dt] = mfma_bf16(av, pb, o[dt]);
-        }
-      } else {
-        // chunk = key tile ch; k-step i: lane group g supplies key 4g+i
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[dt] = mfma_f32(to_f32(vs[4 * g + i][16 * dt + col]), acc[ch][i], o[dt]);
-      }
+        for (int r = 0; r < 4; ++r) o[dt] = mfma_f32(vs[4 * g + r][16 * dt + col], acc[ch][r], o[dt]);
       wave_lds_sync();
     }
   }
-
-  if (col < a.group) {
-    const float inv = 1.f / l_run;
-    TO* orow = reinterpret_cast<TO*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = from_f32<TO>(o[dt][i] * inv);
-    if (a.row_lse && g == 0) {
-      const int hq = a.n_kv_heads * a.group;
-      a.row_lse[((int64_t)b * hq + head) * a.n + t] = m_run + logf(l_run);
-    }
-  }
+  if (col < a.group) finish_row<TO>(a, o, D / 16, m_run, l_run, b, t, head, g);
 }
 
-template <typename T, typename TO, int D>
+template <typename TO, int D>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
-  hipLaunchKernelGGL((attention_kernel<T, TO, D>), grid, dim3(256), 0, s, a);
+  if (a.bf16) {
+    hipLaunchKernelGGL((v_transpose_kernel<D>), dim3(ceil_div(a.n, kLeaf), a.batch * a.n_kv_heads), dim3(256), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attention_f32_kernel<TO, D>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
-template <typename T, typename TO>
+template <typename TO>
 hipError_t launch_attention_o(const AttnArgs& a, hipStream_t s) {
-  return a.head_dim == 64 ? launch_attention_t<T, TO, 64>(a, s) : launch_attention_t<T, TO, 128>(a, s);
+  return a.head_dim == 64 ? launch_attention_t<TO, 64>(a, s) : launch_attention_t<TO, 128>(a, s);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.bf16) return a.out_bf16 ? launch_attention_o<__bf16, __bf16>(a, s) : launch_attention_o<__bf16, float>(a, s);
-  return a.out_bf16 ? launch_attention_o<float, __bf16>(a, s) : launch_attention_o<float, float>(a, s);
+  return a.out_bf16 ? launch_attention_o<__bf16>(a, s) : launch_attention_o<float>(a, s);
 }
 
 }  // namespace pisa

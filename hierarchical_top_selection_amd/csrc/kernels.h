@@ -30,11 +30,17 @@ struct RouteArgs {
   Levels lv;
 };
 
+// Stage-2 work is cut into items of at most kPairsPerItem (token, slot) pairs of one
+// leaf in one window, so a leaf that many queries share is spread over many waves.
+constexpr int kPairsPerItem = 32;
+
 struct ClusterArgs {
   const int32_t* cand;   // [B*Hkv][N][2K]
   int32_t* pairs;        // [B*Hkv][N][2K] packed (t << 6 | slot), grouped by leaf per window
   int32_t* leaf_off;     // [B*Hkv][n_windows][M1 + 1]
-  int batch, n_kv_heads, n, width, n_leaves, window, n_windows;
+  int32_t* items;        // [B*Hkv][n_windows][item_cap] packed (chunk << 16 | leaf)
+  int32_t* n_items;      // [B*Hkv][n_windows]
+  int batch, n_kv_heads, n, width, n_leaves, window, n_windows, item_cap;
 };
 
 struct LeafArgs {
@@ -44,8 +50,10 @@ struct LeafArgs {
   int64_t k_sb, k_st, k_sh;
   const int32_t* pairs;
   const int32_t* leaf_off;
+  const int32_t* items;
+  const int32_t* n_items;
   float* leaf_u;         // [B*Hkv][N][2K]
-  int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows;
+  int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows, item_cap;
   float scale;
   bool bf16;
 };
@@ -69,6 +77,7 @@ struct AttnArgs {
   void* o;
   int64_t o_sb, o_st, o_sh;
   float* row_lse;        // optional [B][Hq][N]
+  __bf16* vt;            // bf16 inputs: workspace for V^T blocks [B*Hkv][M1][d][64]
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
   bool bf16;             // element type of q, k, v

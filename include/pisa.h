@@ -137,23 +137,30 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
                                int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes needed by pisa_sparse_attn_fwd for cfg: bf16 inputs stage V as
+ * transposed 64-key blocks (B * H_kv * ceil(N / 64) * 64 * d * 2 bytes); fp32
+ * inputs need none (0). */
+size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
+
 /*
  * sparse_attn_fwd - causal softmax attention of each query head over the raw
  * keys/values of its group's selected blocks (Prerequisites, block sparse
  * attention; Method steps, fourth step): the key set of token t is the union
  * of blocks in sel[b][kvh][t] cut to positions <= t; fp32 accumulation.
  *   q, k, v : cfg->dtype, shapes as in select_blocks (v like k)
- *   sel     : int32 [B][H_kv][N][K] (any entry < 0 ends nothing: it is skipped;
- *             valid entries must satisfy 64 * j <= t, else the result for that
- *             token is unspecified)
+ *   sel     : int32 [B][H_kv][N][K]; entries < 0 are skipped; valid entries
+ *             must satisfy 64 * j <= t (a block with no key <= t contributes
+ *             nothing; a token with no such block gets a zero row)
  *   o       : [B][N][H_q][d] output of element type o_dtype (float32 keeps the
  *             fp32 accumulator; bfloat16 rounds it to nearest-even)
  *   row_lse : optional float32 [B][H_q][N] output (NULL to skip): natural-log
  *             normaliser of each row's softmax
+ *   ws      : workspace of >= pisa_attn_workspace_bytes(cfg) bytes (may be NULL
+ *             when that is 0), 256-byte aligned
  */
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
-                                 void* stream);
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * decode_step - one autoregressive step for every sequence (Method steps,

@@ -16,7 +16,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_symbols()
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.pisa_abi_version() == 1
@@ -87,4 +87,8 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
                                 None, o, 1, None) == 2
     # output element type must be float32 or bfloat16
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 5,
-                                    None, None) == 1
+                                    None, ctypes.c_void_p(4096), 1 << 30, None) == 1
+    # bf16 attention needs its V^T workspace
+    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == 4096 * 128 * 2
+    assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
+                                    None, None, 0, None) == 3
