@@ -98,7 +98,7 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   w.item_cap = (int)((window_pairs + pisa::kPairsPerItem - 1) / pisa::kPairsPerItem +
                      (m1 < window_pairs ? m1 : window_pairs));
   w.items = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
-  w.n_items = align256(w.items + (size_t)bh * w.n_windows * w.item_cap * 4);
+  w.n_items = align256(w.items + (size_t)bh * w.n_windows * w.item_cap * 8);
   w.total = align256(w.n_items + (size_t)bh * w.n_windows * 4);
   return w;
 }
@@ -168,7 +168,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   float* leaf_u = reinterpret_cast<float*>(base + w.leaf_u);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + w.pairs);
   int32_t* leaf_off = reinterpret_cast<int32_t*>(base + w.leaf_off);
-  int32_t* items = reinterpret_cast<int32_t*>(base + w.items);
+  int2* items = reinterpret_cast<int2*>(base + w.items);
   int32_t* n_items = reinterpret_cast<int32_t*>(base + w.n_items);
   const int N = cfg->seq_len, G = cfg->n_q_heads / cfg->n_kv_heads, width = 2 * cfg->top_k;
   const int m1 = (N + pisa::kLeaf - 1) / pisa::kLeaf;

@@ -6,8 +6,8 @@
 // window's (token, slot) leaf candidates by leaf id entirely in LDS:
 // histogram -> exclusive scan -> scatter.  Output per window: the pairs grouped
 // by leaf (packed t << 6 | slot, stored in the window's own slot range), the
-// M1 + 1 leaf offsets, and the list of work items (chunk << 16 | leaf), each
-// covering at most kPairsPerItem pairs of one leaf.  The order of pairs inside
+// M1 + 1 leaf offsets, and the list of work items {leaf, first pair | count << 20},
+// each covering at most kPairsPerItem pairs of one leaf.  The order of pairs inside
 // one leaf is not fixed (LDS atomics); every pair's score is computed
 // independently, so results do not depend on it.
 #include "kernels.h"
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kClusterThreads) void cluster_kernel(ClusterArgs a)
   int32_t* pairs = a.pairs + ((int64_t)bh * a.n + t0) * a.width;
   const int64_t wid = (int64_t)bh * a.n_windows + w;
   int32_t* off = a.leaf_off + wid * (M + 1);
-  int32_t* work = a.items + wid * a.item_cap;
+  int2* work = a.items + wid * a.item_cap;
 
   for (int i = tid; i < M; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
@@ -77,7 +77,10 @@ __global__ __launch_bounds__(kClusterThreads) void cluster_kernel(ClusterArgs a)
     cnt[i] = run_p;
     off[i] = run_p;
     const int nchunks = (c + kPairsPerItem - 1) / kPairsPerItem;
-    for (int ch = 0; ch < nchunks; ++ch) work[run_i + ch] = (ch << 16) | i;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int first = run_p + ch * kPairsPerItem;
+      work[run_i + ch] = make_int2(i, first | (min(kPairsPerItem, c - ch * kPairsPerItem) << 20));
+    }
     run_p += c;
     run_i += nchunks;
   }

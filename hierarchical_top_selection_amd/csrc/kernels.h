@@ -38,7 +38,7 @@ struct ClusterArgs {
   const int32_t* cand;   // [B*Hkv][N][2K]
   int32_t* pairs;        // [B*Hkv][N][2K] packed (t << 6 | slot), grouped by leaf per window
   int32_t* leaf_off;     // [B*Hkv][n_windows][M1 + 1]
-  int32_t* items;        // [B*Hkv][n_windows][item_cap] packed (chunk << 16 | leaf)
+  int2* items;           // [B*Hkv][n_windows][item_cap] {leaf, first pair | count << 20}
   int32_t* n_items;      // [B*Hkv][n_windows]
   int batch, n_kv_heads, n, width, n_leaves, window, n_windows, item_cap;
 };
@@ -50,7 +50,7 @@ struct LeafArgs {
   int64_t k_sb, k_st, k_sh;
   const int32_t* pairs;
   const int32_t* leaf_off;
-  const int32_t* items;
+  const int2* items;
   const int32_t* n_items;
   float* leaf_u;         // [B*Hkv][N][2K]
   int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows, item_cap;

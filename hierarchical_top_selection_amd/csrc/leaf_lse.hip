@@ -2,11 +2,10 @@
 // Stage 2; Core method eq. 21 at the leaf level; Method steps eq. 22 head sum of
 // "Block Sparse Attention with Log-Linear Complexity").
 //
-// Leaf-major: a wave takes one work item (one leaf of one token window, at most
-// kPairsPerItem queries).  The leaf's 64 keys are loaded once into MFMA A
-// fragments held in registers (bf16: 64 VGPRs at d = 128) and reused by every
-// query of the item; each query streams in only its G head rows (the B tile),
-// prefetched three queries ahead.  The product is kept transposed, S^T = K Q^T
+// Leaf-major: a wave walks a few work items (each one leaf of one token window,
+// at most kPairsPerItem queries).  The leaf's 64 keys are loaded once into MFMA
+// A fragments held in registers (bf16: 64 VGPRs at d = 128) and reused by every
+// query of the item; each query streams in only its G head rows (the B tile).  The product is kept transposed, S^T = K Q^T
 // (keys on rows, heads on columns), so a lane owns 16 keys of one head: the
 // per-head max and sum over the 64 keys are in-lane plus two cross-group
 // shuffles, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
@@ -21,10 +20,12 @@ namespace pisa {
 // walks windows x, x + 8, x + 16, ... so one window's query rows stay in one L2.
 constexpr int kXcds = 8;
 
+constexpr int kItemsPerWave = 4;
+
 template <typename T, int D>
 __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], const typename RawFrag<T, D>::type& qf,
-                                 int packed, const LeafArgs& a, int64_t leaf_first, bool edge_leaf, float c2,
-                                 bool head_ok, int g, int lane, float* uout) {
+                                 int packed, const LeafArgs& a, int start, int last, float c2, bool head_ok,
+                                 int g, int lane, float* uout) {
   const int t = packed >> 6, slot = packed & 63;
   floatx4 acc[4];
 #pragma unroll
@@ -32,15 +33,15 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     acc[mt] = mma(kf[mt], qf, acc[mt]);
   }
-  // acc[mt][r]: key leaf_first + 16 mt + 4 g + r against head column col
-  if (leaf_first + kLeaf - 1 > t || edge_leaf) {
+  // acc[mt][r]: key (start + 16 mt + 4 g + r) against head column col.  Keys past
+  // min(t, n - 1) are masked; `last` is n - 1 - start capped at 63.
+  const int lim = min(t - start, last);
+  if (lim < kLeaf - 1) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = leaf_first + 16 * mt + 4 * g + r;
-        if (key > t || key >= a.n) acc[mt][r] = kNegInf;
-      }
+      for (int r = 0; r < 4; ++r)
+        if (16 * mt + 4 * g + r > lim) acc[mt][r] = kNegInf;
   }
   float m = kNegInf;
 #pragma unroll
@@ -57,8 +58,8 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
   s = wave_add_xor(s, 16);
   s = wave_add_xor(s, 32);
-  // natural-log LSE of this head: (m c2 + log2 s) ln 2
-  float u = head_ok ? (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f : 0.f;   // s >= 1: no denormal fix-up needed
+  // natural-log LSE of this head: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
+  float u = head_ok ? (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f : 0.f;
   u = wave_add_xor(u, 1);
   u = wave_add_xor(u, 2);
   u = wave_add_xor(u, 4);
@@ -66,68 +67,81 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
   if (lane == 0) uout[(int64_t)t * a.width + slot] = u;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void leaf_lse_kernel(LeafArgs a) {
+// Each wave walks kItemsPerWave consecutive items of one window.  The next item's
+// record and query list are fetched one item ahead, the query rows one query ahead
+// (across item boundaries), and consecutive items of the same leaf keep their keys.
+// fp32 keys at d = 128 need 128 VGPRs of fragments: no occupancy target there.
+template <typename T, int D, int kWaves = (sizeof(T) == 4 && D == 128) ? 1 : 3>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) void leaf_lse_kernel(LeafArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int blocks_per_window = ceil_div(a.item_cap, 4);
+  const int blocks_per_window = ceil_div(a.item_cap, 4 * kItemsPerWave);
   const int xcd = blockIdx.x % kXcds, slot_id = blockIdx.x / kXcds;
   const int64_t wid = (int64_t)kXcds * (slot_id / blocks_per_window) + xcd;   // bh * n_windows + w
   if (wid >= (int64_t)a.batch * a.n_kv_heads * a.n_windows) return;
-  const int item = (slot_id % blocks_per_window) * 4 + wave;
-  if (item >= a.n_items[wid]) return;
+  const int it0 = ((slot_id % blocks_per_window) * 4 + wave) * kItemsPerWave;
+  const int it_end = min(it0 + kItemsPerWave, a.n_items[wid]);
+  if (it0 >= it_end) return;
   const int bh = (int)(wid / a.n_windows), w = (int)(wid % a.n_windows);
-  const int code = a.items[wid * a.item_cap + item];
-  const int leaf = code & 0xffff, chunk = code >> 16;
-  const int32_t* off = a.leaf_off + wid * (a.n_leaves + 1);
-  const int p0 = off[leaf] + chunk * kPairsPerItem;
-  const int np = min(kPairsPerItem, off[leaf + 1] - p0);
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int g = lane >> 4, col = lane & 15;
-
-  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.k_sb + kvh * a.k_sh;
-  const int64_t leaf_first = (int64_t)leaf * kLeaf;
-  Frag kf[4];                                          // rows past the end are clamped, then masked
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(leaf_first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+  const int2* items = a.items + wid * a.item_cap;
   const int32_t* pairs = a.pairs + ((int64_t)bh * a.n + (int64_t)w * a.window) * a.width;
-  const int my_pair = lane < np ? pairs[p0 + lane] : 0;
+  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.k_sb + kvh * a.k_sh;
   const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)(kvh * a.group + col) * a.q_sh;
   float* uout = a.leaf_u + (int64_t)bh * a.n * a.width;
   const float c2 = a.scale * 1.4426950408889634f;      // logits in base-2 units
   const bool head_ok = col < a.group;
-  const bool edge_leaf = leaf_first + kLeaf > a.n;     // last, partial leaf
 
-  // query rows of pair i, prefetched three pairs ahead through a ring of four fragments
-  auto load_q = [&](Frag& f, int i) {
-    if (i < np) {
-      const int t = __shfl(my_pair, i, 64) >> 6;
-      if (head_ok) f.load(qbase + (int64_t)t * a.q_st, g); else f.zero();
-    }
+  auto item_pairs = [&](int2 rec) {
+    const int np = rec.y >> 20, p0 = rec.y & 0xfffff;
+    return lane < np ? pairs[p0 + lane] : 0;
   };
-  Frag q0, q1, q2, q3;
-  load_q(q0, 0);
-  load_q(q1, 1);
-  load_q(q2, 2);
-  for (int i = 0; i < np; i += 4) {
-    load_q(q3, i + 3);
-    leaf_pair<T, D>(kf, q0, __shfl(my_pair, i, 64), a, leaf_first, edge_leaf, c2, head_ok, g, lane, uout);
-    if (i + 1 >= np) break;
-    load_q(q0, i + 4);
-    leaf_pair<T, D>(kf, q1, __shfl(my_pair, i + 1, 64), a, leaf_first, edge_leaf, c2, head_ok, g, lane, uout);
-    if (i + 2 >= np) break;
-    load_q(q1, i + 5);
-    leaf_pair<T, D>(kf, q2, __shfl(my_pair, i + 2, 64), a, leaf_first, edge_leaf, c2, head_ok, g, lane, uout);
-    if (i + 3 >= np) break;
-    load_q(q2, i + 6);
-    leaf_pair<T, D>(kf, q3, __shfl(my_pair, i + 3, 64), a, leaf_first, edge_leaf, c2, head_ok, g, lane, uout);
+  auto load_q = [&](Frag& f, int packed) {
+    if (head_ok) f.load(qbase + (int64_t)(packed >> 6) * a.q_st, g); else f.zero();
+  };
+
+  int2 rec = items[it0];
+  int2 rec_n = it0 + 1 < it_end ? items[it0 + 1] : make_int2(-1, 0);
+  int pr = item_pairs(rec);
+  int pr_n = it0 + 1 < it_end ? item_pairs(rec_n) : 0;
+  Frag kf[4];
+  int cur_leaf = -1;
+  Frag q0, q1;
+  load_q(q0, __shfl(pr, 0, 64));
+  for (int it = it0; it < it_end; ++it) {
+    const int leaf = rec.x, np = rec.y >> 20;
+    const int2 rec_nn = it + 2 < it_end ? items[it + 2] : make_int2(-1, 0);
+    if (leaf != cur_leaf) {                            // rows past the end are clamped, then masked
+      const int64_t first = (int64_t)leaf * kLeaf;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+      cur_leaf = leaf;
+    }
+    const int start = leaf * kLeaf;
+    const int last = min(kLeaf - 1, a.n - 1 - start);   // last key of this leaf, relative to its start
+    for (int i = 0; i < np; ++i) {
+      // rows of the following query (this item's next, or the next item's first)
+      const bool in_item = i + 1 < np;
+      const bool have_next = in_item || it + 1 < it_end;
+      const int nxt = __shfl(in_item ? pr : pr_n, in_item ? i + 1 : 0, 64);
+      if (have_next) load_q(q1, nxt);
+      leaf_pair<T, D>(kf, q0, __shfl(pr, i, 64), a, start, last, c2, head_ok, g, lane, uout);
+      q0 = q1;
+    }
+    if (it + 1 < it_end) {
+      rec = rec_n;
+      pr = pr_n;
+      rec_n = rec_nn;
+      pr_n = it + 2 < it_end ? item_pairs(rec_n) : 0;
+    }
   }
 }
 
 template <typename T, int D>
 hipError_t launch_leaf_t(const LeafArgs& a, hipStream_t s) {
   const int64_t windows = (int64_t)a.batch * a.n_kv_heads * a.n_windows;
-  const int64_t blocks = kXcds * ((windows + kXcds - 1) / kXcds) * ceil_div(a.item_cap, 4);
+  const int64_t blocks = kXcds * ((windows + kXcds - 1) / kXcds) * ceil_div(a.item_cap, 4 * kItemsPerWave);
   hipLaunchKernelGGL((leaf_lse_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -61,6 +61,9 @@ __device__ inline float4 load4(const __bf16* p) {
 // feed k-steps 4 m + j.
 template <int D>
 struct FragF32 {
+  static constexpr int kVecs = D / 16;       // 16-byte pieces per lane
+  // element offset (within a row) of piece m for lane group g
+  __host__ __device__ static constexpr int piece_offset(int m, int g) { return 16 * m + 4 * g; }
   float4 v[D / 16];
   template <typename T>
   __device__ inline void load(const T* row, int g) {
@@ -76,6 +79,9 @@ struct FragF32 {
 // Row fragment for the bf16 MFMA (16x16x32): k-step s covers indices 32 s + 8 g + j.
 template <int D>
 struct FragBF16 {
+  static constexpr int kVecs = D / 32;       // 16-byte pieces per lane
+  // element offset (within a row) of piece s for lane group g
+  __host__ __device__ static constexpr int piece_offset(int s, int g) { return 32 * s + 8 * g; }
   bf16x8 v[D / 32];
   __device__ inline void load(const __bf16* row, int g) {
 #pragma unroll
