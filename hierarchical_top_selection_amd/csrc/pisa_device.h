@@ -130,6 +130,16 @@ template <int D> struct RawFrag<__bf16, D> { typedef FragBF16<D> type; };
 __device__ inline float wave_max_xor(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask, 64)); }
 __device__ inline float wave_add_xor(float x, int mask) { return x + __shfl_xor(x, mask, 64); }
 
+// Sum over the 16 lanes of each row (lanes 16 r .. 16 r + 15) with DPP row shifts;
+// the row total lands in the row's last lane (lane 16 r + 15).
+__device__ inline float row_sum_to_last(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+  return x;
+}
+
 // Orders this wave's LDS writes before its later LDS reads of other lanes' data
 // (wave-private staging buffers; no workgroup barrier needed).
 __device__ inline void wave_lds_sync() {

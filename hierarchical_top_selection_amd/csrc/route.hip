@@ -2,21 +2,30 @@
 // pyramid levels above the leaves (Core method eq. 16-21; Method steps eq. 22 of
 // "Block Sparse Attention with Log-Linear Complexity").
 //
-// One wave routes one (b, kvh, token).  The G query heads of the group are the
-// 16 rows of an fp32 MFMA A tile (rows >= G are zero); the candidates' children
-// are gathered 16 at a time as the B tile, so one MFMA pass yields the logits of
-// every head against 16 children.  Candidate lists never leave registers: lane
+// One wave routes one (b, kvh, token).  The candidates' children are gathered 16
+// at a time as the rows of an MFMA A tile and the group's G query heads are the
+// columns of the B tile (columns >= G are zero), so one MFMA pass yields the
+// logits of every head against 16 children, and a candidate's two children land
+// in the same lane.  Candidate lists never leave registers: lane
 // i owns candidate i, a level keeps K of them by exact rank (score descending,
 // node index ascending) and the survivors expand into the next list with a
 // ballot/bit-select compaction.  The leaf candidates (at most 2K per token) are
-// the only output.  The pyramid is float32 and the products are fp32 MFMA, so
-// the scores carry full single precision.
+// the only output.
+//
+// Scores need full single precision (near-ties between candidates are common),
+// so the summaries stay float32 and the products run on v_mfma_f32_16x16x4_f32
+// (bf16 queries are widened exactly).  The kernel is bound by gathering summary
+// rows (8 KB per 16-child tile), so each tile's rows are requested one tile
+// ahead.  (Splitting each summary into three bf16 terms would cut the MFMA
+// cycles fivefold but gathers 1.5x the bytes, and measured slower.)  The LSE of
+// a candidate's two children is evaluated in base 2 as max + log2(1 + 2^-|diff|)
+// on pre-scaled logits.
 #include "kernels.h"
 
 namespace pisa {
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
@@ -24,6 +33,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int g = lane >> 4, col = lane & 15;
   const int width = 2 * a.top_k;
+  const float c2 = a.scale * 1.4426950408889634f;       // logits in base-2 units
 
   FragF32<D> qf;
   if (col < a.group) {
@@ -40,36 +50,52 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const uint64_t valid = __ballot(cand >= 0);
     const int n_valid = __popcll(valid);
     const int child_size = a.lv.size[level - 2];
-    const float* child_base = pyr + a.lv.offset[level - 2] * D;
+    const int64_t child_off = a.lv.offset[level - 2];
     bool keep = cand >= 0;
     if (n_valid > a.top_k) {
       const int span = 64 - __clzll(valid);            // highest occupied lane + 1
       const int tiles = (2 * span + 15) / 16;
-      float u = kNegInf;                               // score of candidate `lane`
-      for (int nt = 0; nt < tiles; ++nt) {
-        const int slot = 16 * nt + col;                // child slot: candidate slot/2, child slot&1
+      // child of tile nt owned by this lane's row index: candidate slot/2, child slot&1.  Rows of
+      // invalid children load a clamped row and are masked.
+      auto child_of = [&](int nt, bool& ok) {
+        const int slot = 16 * nt + col;
         const int parent = __shfl(cand, slot >> 1, 64);
         const int child = 2 * parent + (slot & 1);
-        const bool ok = parent >= 0 && child < child_size && node_first_key(level - 1, child) <= t;
-        FragF32<D> kf;
-        if (ok) kf.load(child_base + (int64_t)child * D, g); else kf.zero();
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(qf, kf, acc);
-        // rows 4g+i are heads, column col is this child; pair children 2c, 2c+1 are lanes col, col^1
-        float head_sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float z = ok ? acc[i] * a.scale : kNegInf;
-          const float zp = __shfl_xor(z, 1, 64);
-          const float m = fmaxf(z, zp);
-          const float s = m == kNegInf ? kNegInf : m + logf(expf(z - m) + expf(zp - m));
-          if (4 * g + i < a.group) head_sum += s;
+        ok = parent >= 0 && child < child_size && node_first_key(level - 1, child) <= t;
+        return ok ? child : 0;
+      };
+      float u = kNegInf;                               // score of candidate `lane` (base 2)
+      bool ok_n;
+      int child_n = child_of(0, ok_n);
+      FragF32<D> kf_n;
+      kf_n.load(pyr + (child_off + child_n) * D, g);
+      for (int nt = 0; nt < tiles; ++nt) {
+        const FragF32<D> kf = kf_n;
+        // validity of the children this lane holds results for: rows 4g .. 4g+3 of the tile
+        const uint64_t okmask = __ballot(ok_n);
+        if (nt + 1 < tiles) {                          // next tile's rows in flight during this one
+          child_n = child_of(nt + 1, ok_n);
+          kf_n.load(pyr + (child_off + child_n) * D, g);
         }
-        head_sum += __shfl_xor(head_sum, 16, 64);
-        head_sum += __shfl_xor(head_sum, 32, 64);
-        // lane 2c of any group now holds candidate 8 nt + c's score
-        const float got = __shfl(head_sum, 2 * (lane & 7), 64);
-        if ((lane >> 3) == nt) u = got;
+        // S^T tile: rows = 16 children, columns = heads; lane (g, col) gets children 4g + i of head col
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma(kf, qf, acc);
+        float pair_score[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                  // candidate 8 nt + 2g + h: children rows 4g + 2h, +1
+          const int r0 = 4 * g + 2 * h;
+          const float z0 = ((okmask >> r0) & 1) ? acc[2 * h] * c2 : kNegInf;
+          const float z1 = ((okmask >> (r0 + 1)) & 1) ? acc[2 * h + 1] * c2 : kNegInf;
+          const float m = fmaxf(z0, z1);
+          const float sc = m == kNegInf ? kNegInf
+                                        : m + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(z0, z1) - m));
+          pair_score[h] = row_sum_to_last(col < a.group ? sc : 0.f);   // sum over the group's heads
+        }
+        // lane 16 g + 15 holds candidates 8 nt + 2 g and 8 nt + 2 g + 1
+        const int src = 16 * ((lane & 7) >> 1) + 15;
+        const float s0 = __shfl(pair_score[0], src, 64);
+        const float s1 = __shfl(pair_score[1], src, 64);
+        if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
       }
       int rank = 0;
       for (int j = 0; j < span; ++j) {
