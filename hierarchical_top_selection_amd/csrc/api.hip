@@ -79,7 +79,7 @@ pisa_status hip_status(hipError_t e) {
 }
 
 struct SelectWorkspace {
-  size_t cand, leaf_u, pairs, leaf_off, items, n_items, total;
+  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, total;
   int n_windows, item_cap;
 };
 
@@ -99,7 +99,10 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
                      (m1 < window_pairs ? m1 : window_pairs));
   w.items = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
   w.n_items = align256(w.items + (size_t)bh * w.n_windows * w.item_cap * 8);
-  w.total = align256(w.n_items + (size_t)bh * w.n_windows * 4);
+  w.split = align256(w.n_items + (size_t)bh * w.n_windows * 4);
+  // bf16 inputs: split summaries for routing, 4 bytes per pyramid element
+  const size_t split_bytes = c->dtype == PISA_BF16 ? (size_t)bh * make_levels(c->seq_len, c->seq_len).nodes * c->head_dim * 4 : 0;
+  w.total = align256(w.split + split_bytes);
   return w;
 }
 
@@ -182,6 +185,9 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.batch = cfg->batch; r.n_kv_heads = cfg->n_kv_heads; r.group = G; r.head_dim = cfg->head_dim;
   r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16;
   r.lv = make_levels(N, N);
+  r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
+  if (bf16 && (st = hip_status(pisa::launch_split_summaries(r, (int64_t)cfg->batch * cfg->n_kv_heads * r.lv.nodes, s))) != PISA_OK)
+    return st;
   if ((st = hip_status(pisa::launch_route(r, s))) != PISA_OK) return st;
 
   pisa::ClusterArgs c;

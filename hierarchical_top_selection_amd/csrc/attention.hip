@@ -199,15 +199,16 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     }
     if (more) load_k(leaf_n);                          // K of the next block into the freed fragments
 
-    // acc[mt][r]: key first + perm_key(mt, 4 g + r) against head column col
-    if (first + kLeaf - 1 > t || first + kLeaf > a.n) {
+    // acc[mt][r]: key first + perm_key(mt, 4 g + r) against head column col.  Only a block that
+    // reaches past t needs a mask; t < n, so that also masks keys past the end.  The key offset
+    // 32 (mt / 2) + 8 g + 4 (mt % 2) + r is compared with t - first - 8 g in 32 bits.
+    if (first + kLeaf - 1 > t) {
+      const int lim = t - (int)first - 8 * g;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = first + perm_key(mt, 4 * g + r);
-          if (key > t || key >= a.n) acc[mt][r] = kNegInf;
-        }
+        for (int r = 0; r < 4; ++r)
+          if (32 * (mt >> 1) + 4 * (mt & 1) + r > lim) acc[mt][r] = kNegInf;
     }
     float tmax = kNegInf;
 #pragma unroll

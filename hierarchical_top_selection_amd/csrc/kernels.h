@@ -23,6 +23,7 @@ struct RouteArgs {
   const void* q;
   int64_t q_sb, q_st, q_sh;
   const float* pyr;
+  uint16_t* split;        // bf16 inputs: [B*Hkv][nodes][2 d] summaries as bf16 high parts, then f16 remainders
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
@@ -108,6 +109,8 @@ struct DecodeArgs {
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// bf16 inputs: fills a.split from a.pyr for `rows` summary rows (B*Hkv*nodes).
+hipError_t launch_split_summaries(const RouteArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);

@@ -23,6 +23,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ----------------------------------------------------------------------------- geometry
 // Level sizes for the current length and node offsets for the capacity layout.
@@ -95,6 +96,16 @@ struct FragBF16 {
   }
 };
 
+// Row fragment for the f16 MFMA (16x16x32): same element placement as FragBF16.
+template <int D>
+struct FragF16 {
+  f16x8 v[D / 32];
+  __device__ inline void load(const _Float16* row, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) v[s] = *reinterpret_cast<const f16x8*>(row + 32 * s + 8 * g);
+  }
+};
+
 __device__ inline floatx4 mfma_f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -118,6 +129,12 @@ template <int D>
 __device__ inline floatx4 mma(const FragBF16<D>& a, const FragBF16<D>& b, floatx4 acc) {
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) acc = mfma_bf16(a.v[s], b.v[s], acc);
+  return acc;
+}
+template <int D>
+__device__ inline floatx4 mma(const FragF16<D>& a, const FragF16<D>& b, floatx4 acc) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v[s], b.v[s], acc, 0, 0, 0);
   return acc;
 }
 

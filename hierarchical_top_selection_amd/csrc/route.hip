@@ -12,18 +12,101 @@
 // ballot/bit-select compaction.  The leaf candidates (at most 2K per token) are
 // the only output.
 //
-// Scores need full single precision (near-ties between candidates are common),
-// so the summaries stay float32 and the products run on v_mfma_f32_16x16x4_f32
-// (bf16 queries are widened exactly).  The kernel is bound by gathering summary
-// rows (8 KB per 16-child tile), so each tile's rows are requested one tile
-// ahead.  (Splitting each summary into three bf16 terms would cut the MFMA
-// cycles fivefold but gathers 1.5x the bytes, and measured slower.)  The LSE of
-// a candidate's two children is evaluated in base 2 as max + log2(1 + 2^-|diff|)
-// on pre-scaled logits.
+// Scores need close to single precision (near-ties between candidates are
+// common).  fp32 queries use fp32 summaries on v_mfma_f32_16x16x4_f32.  bf16
+// queries are exact in bf16 and in f16, so each fp32 summary x is split once
+// into hi = bf16(x) and lo = f16((x - hi) 2^10) (the remainder's 8 + 11 bits
+// leave a relative error of about 2^-20 per element) and q . x = q . hi +
+// 2^-10 q . lo runs on the 16-cycle bf16 and f16 16x16x32 MFMAs: 8 instead of
+// 32 fp32 MFMAs per tile, from the same 4 bytes per element.  The kernel
+// gathers summary rows (8 KB per 16-child tile), so each tile's rows are
+// requested one tile ahead.  The LSE of a candidate's two children is evaluated
+// in base 2 as max + log2(1 + 2^-|diff|) on pre-scaled logits.
 #include "kernels.h"
 
 namespace pisa {
 
+// ----------------------------------------------------------------------------- operands
+// Query operands (B tile columns) and summary tiles (A tile rows) of one precision.
+template <typename T, int D> struct RouteOps;
+
+template <int D> struct RouteOps<float, D> {         // fp32 summaries, fp32 MFMA
+  typedef float Row;
+  static constexpr int kRowElems = D;
+  struct Q { FragF32<D> f; };
+  struct Tile {
+    FragF32<D> f;
+    __device__ inline void load(const Row* rows, int64_t node, int g) { f.load(rows + node * kRowElems, g); }
+  };
+  __device__ static inline void load_q(Q& q, const float* row, int g) { q.f.load(row, g); }
+  __device__ static inline void zero_q(Q& q) { q.f.zero(); }
+  __device__ static inline const Row* rows(const RouteArgs& a) { return a.pyr; }
+  __device__ static inline floatx4 dot(const Tile& t, const Q& q) {
+    return mma(t.f, q.f, floatx4{0.f, 0.f, 0.f, 0.f});
+  }
+};
+
+template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 remainder
+  typedef uint16_t Row;
+  static constexpr int kRowElems = 2 * D;
+  struct Q { FragBF16<D> h; FragF16<D> l; };
+  struct Tile {
+    FragBF16<D> h;
+    FragF16<D> l;
+    __device__ inline void load(const Row* rows, int64_t node, int g) {
+      const Row* r = rows + node * kRowElems;
+      h.load(reinterpret_cast<const __bf16*>(r), g);
+      l.load(reinterpret_cast<const _Float16*>(r + D), g);
+    }
+  };
+  // bf16 values are exact in f16 up to its range; larger ones saturate
+  __device__ static inline void load_q(Q& q, const __bf16* row, int g) {
+    q.h.load(row, g);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q.l.v[s][j] = (_Float16)fminf(fmaxf((float)q.h.v[s][j], -65504.f), 65504.f);
+  }
+  __device__ static inline void zero_q(Q& q) {
+    q.h.zero();
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q.l.v[s][j] = (_Float16)0.f;
+  }
+  __device__ static inline const Row* rows(const RouteArgs& a) { return a.split; }
+  __device__ static inline floatx4 dot(const Tile& t, const Q& q) {
+    const floatx4 hi = mma(t.h, q.h, floatx4{0.f, 0.f, 0.f, 0.f});
+    const floatx4 lo = mma(t.l, q.l, floatx4{0.f, 0.f, 0.f, 0.f});
+    return hi + lo * 0.0009765625f;                   // 2^-10
+  }
+};
+
+// Row r of the split layout: [bf16(x) for the d elements][f16((x - bf16(x)) 2^10)], each
+// conversion to nearest, the remainder clamped to the f16 range.  One thread per 8 elements.
+template <int D>
+__global__ __launch_bounds__(256) void split_summaries_kernel(const float* pyr, uint16_t* out, int64_t rows) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = e / (D / 8);
+  const int c8 = (int)(e % (D / 8));
+  if (row >= rows) return;
+  const float4 a = *reinterpret_cast<const float4*>(pyr + row * D + 8 * c8);
+  const float4 b = *reinterpret_cast<const float4*>(pyr + row * D + 8 * c8 + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  bf16x8 hi;
+  f16x8 lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    hi[j] = (__bf16)x[j];
+    const float r = (x[j] - (float)hi[j]) * 1024.f;  // exact: x and hi agree to 8 bits
+    lo[j] = (_Float16)fminf(fmaxf(r, -65504.f), 65504.f);
+  }
+  uint16_t* dst = out + row * 2 * D;
+  *reinterpret_cast<bf16x8*>(dst + 8 * c8) = hi;
+  *reinterpret_cast<f16x8*>(dst + D + 8 * c8) = lo;
+}
+
+// ----------------------------------------------------------------------------- routing
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -35,15 +118,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   const int width = 2 * a.top_k;
   const float c2 = a.scale * 1.4426950408889634f;       // logits in base-2 units
 
-  FragF32<D> qf;
+  typedef RouteOps<T, D> Ops;
+  typename Ops::Q qf;
   if (col < a.group) {
     const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st +
                     (int64_t)(kvh * a.group + col) * a.q_sh;
-    qf.load(qrow, g);
+    Ops::load_q(qf, qrow, g);
   } else {
-    qf.zero();
+    Ops::zero_q(qf);
   }
-  const float* pyr = a.pyr + (int64_t)bh * a.lv.nodes * D;
+  const typename Ops::Row* rows = Ops::rows(a) + (int64_t)bh * a.lv.nodes * Ops::kRowElems;
 
   int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
   for (int level = a.lv.count; level >= 2; --level) {
@@ -67,19 +151,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       float u = kNegInf;                               // score of candidate `lane` (base 2)
       bool ok_n;
       int child_n = child_of(0, ok_n);
-      FragF32<D> kf_n;
-      kf_n.load(pyr + (child_off + child_n) * D, g);
+      typename Ops::Tile kf_n;
+      kf_n.load(rows, child_off + child_n, g);
       for (int nt = 0; nt < tiles; ++nt) {
-        const FragF32<D> kf = kf_n;
+        const typename Ops::Tile kf = kf_n;
         // validity of the children this lane holds results for: rows 4g .. 4g+3 of the tile
         const uint64_t okmask = __ballot(ok_n);
         if (nt + 1 < tiles) {                          // next tile's rows in flight during this one
           child_n = child_of(nt + 1, ok_n);
-          kf_n.load(pyr + (child_off + child_n) * D, g);
+          kf_n.load(rows, child_off + child_n, g);
         }
         // S^T tile: rows = 16 children, columns = heads; lane (g, col) gets children 4g + i of head col
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(kf, qf, acc);
+        const floatx4 acc = Ops::dot(kf, qf);
         float pair_score[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {                  // candidate 8 nt + 2g + h: children rows 4g + 2h, +1
@@ -121,6 +204,16 @@ template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
   hipLaunchKernelGGL((route_kernel<T, D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_summaries(const RouteArgs& a, int64_t rows, hipStream_t s) {
+  const int64_t threads = rows * (a.head_dim / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(split_summaries_kernel<64>, dim3(blocks), dim3(256), 0, s, a.pyr, a.split, rows);
+  else
+    hipLaunchKernelGGL(split_summaries_kernel<128>, dim3(blocks), dim3(256), 0, s, a.pyr, a.split, rows);
   return hipGetLastError();
 }
 

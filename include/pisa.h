@@ -125,14 +125,19 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  * i * 64 * 2^(l-1) <= t), keeps K by (u descending, index ascending) and
  * expands the survivors to their valid children.  The leaf level scores the
  * at most 2K candidate leaves exactly over their raw keys at positions <= t.
+ * Precision: products of raw inputs are exact with float32 sums.  For bf16
+ * inputs the float32 summaries above the leaves enter the dot products as a
+ * bf16 part plus a float16 remainder scaled by 2^10 (about 2^-20 relative
+ * error per element); float32 inputs use the summaries as they are.
  *   q, k    : [B][N][H_q][d] and [B][N][H_kv][d], cfg->dtype
  *   pyr     : pyramid of k built with n = N (capacity N)
  *   sel     : int32 [B][H_kv][N][K] output, ascending, -1 padded
  *   sel_u   : optional float32 [B][H_kv][N][K] output (NULL to skip): the leaf
  *             score u of each selected block, -inf on padding
- *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes; its
- *             first B*H_kv*N*2K int32 hold the leaf candidates of each token
- *             (-1 padded) after the call
+ *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes (it
+ *             also holds the split summaries of bf16 inputs); its first
+ *             B*H_kv*N*2K int32 hold the leaf candidates of each token (-1
+ *             padded) after the call
  */
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
                                int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
