@@ -217,7 +217,7 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg) {
   if (check_cfg(cfg) != PISA_OK) return 0;
   if (cfg->dtype != PISA_BF16) return 0;
   const int64_t m1 = (cfg->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
-  return align256((size_t)cfg->batch * cfg->n_kv_heads * m1 * pisa::kLeaf * cfg->head_dim * 2);
+  return 2 * align256((size_t)cfg->batch * cfg->n_kv_heads * m1 * pisa::kLeaf * cfg->head_dim * 2);
 }
 
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
@@ -240,7 +240,8 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.sel = sel;
   a.o = o.ptr; a.o_sb = o.stride_b; a.o_st = o.stride_t; a.o_sh = o.stride_h;
   a.row_lse = row_lse;
-  a.vt = static_cast<__bf16*>(ws);
+  a.kpack = static_cast<pisa::bf16x8*>(ws);
+  a.vpack = a.kpack + need / 2 / sizeof(pisa::bf16x8);
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
   a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = o_dtype == PISA_BF16;

@@ -9,14 +9,14 @@
 // logits), and accumulates O^T += V_j^T P^T.  Keeping S transposed makes P^T's
 // B fragment exactly the lane's own accumulator values.
 //
-// The kernel is bound by gathering K/V blocks from memory.  The bf16 path first
-// writes V transposed per leaf block (one cheap pass over V), loads the K rows
-// of each block in a permuted key order, and thereby gets both PV operands as
-// plain 16-byte loads straight into MFMA fragments -- no LDS at all.  It is
-// software-pipelined one block ahead: as soon as the S^T MFMAs have consumed
-// K_j (and the PV MFMAs V_j), the registers are refilled for block j+1, so the
-// gather latency overlaps the softmax and MFMA work.  fp32 inputs take a plain
-// path that stages V through LDS, on v_mfma_f32_16x16x4_f32.
+// The kernel is bound by gathering K/V blocks from memory.  The bf16 path reads
+// K and V from packed blocks (one cheap pass over K and V, pack.hip): every MFMA
+// fragment, including V^T's and the K rows in the permuted key order that makes
+// P^T a lane's own values, is one contiguous 1 KB load straight into registers --
+// no LDS at all.  It is software-pipelined one block ahead: as soon as the S^T
+// MFMAs have consumed K_j (and the PV MFMAs V_j), the registers are refilled for
+// block j+1, so the gather latency overlaps the softmax and MFMA work.  fp32
+// inputs take a plain path that stages V through LDS, on v_mfma_f32_16x16x4_f32.
 #include "kernels.h"
 
 namespace pisa {
@@ -95,39 +95,6 @@ __device__ inline void finish_row(const AttnArgs& a, const floatx4* o, int nd16,
 }  // namespace
 
 // ----------------------------------------------------------------------------- bf16, pipelined
-// V^T blocks: vt[bh][leaf][c][64 keys] (keys past n are zero), so an 8-key run of one
-// value column is one 16-byte load.
-template <int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(AttnArgs a) {
-  __shared__ __bf16 tile[kLeaf][D + 8];
-  const int leaf = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh;
-  const int64_t first = (int64_t)leaf * kLeaf;
-  for (int e = threadIdx.x; e < kLeaf * D / 8; e += blockDim.x) {
-    const int r = e / (D / 8), cv = e % (D / 8);
-    const int64_t key = first + r;
-    const uint4 val = key < a.n ? *reinterpret_cast<const uint4*>(vbase + key * a.v_st + cv * 8)
-                                : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&tile[r][cv * 8]) = val;
-  }
-  __syncthreads();
-  const int m1 = ceil_div(a.n, kLeaf);
-  __bf16* dst = a.vt + (((int64_t)bh * m1 + leaf) * D) * kLeaf;
-  for (int e = threadIdx.x; e < D * kLeaf / 8; e += blockDim.x) {
-    const int c = e / (kLeaf / 8), k8 = e % (kLeaf / 8);
-    bf16x8 out;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = tile[8 * k8 + i][c];
-    *reinterpret_cast<bf16x8*>(dst + (int64_t)c * kLeaf + 8 * k8) = out;
-  }
-}
-
-// Key order inside a block: M-tile mt = 2 kb + h, row m holds key 32 kb + 8 (m / 4) + 4 h + m % 4,
-// so in the S^T result lane group g of tiles (2 kb, 2 kb + 1) owns keys 32 kb + 8 g + 0..7 -- exactly
-// the k-slice that the lane supplies for the P V product of key half kb.
-__device__ inline int perm_key(int mt, int m) { return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3); }
-
 template <typename TO, int D>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   typedef FragBF16<D> Frag;
@@ -145,8 +112,8 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     qf.load(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st + (int64_t)head * a.q_sh, g);
   else
     qf.zero();
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh;
-  const __bf16* vtbase = a.vt + (int64_t)bh * m1 * D * kLeaf;
+  const bf16x8* kpack = a.kpack + (int64_t)bh * m1 * (kLeaf * D / 8);
+  const bf16x8* vpack = a.vpack + (int64_t)bh * m1 * (kLeaf * D / 8);
   const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
   const uint64_t valid = __ballot(my_sel >= 0);        // entries < 0 are skipped
   const int nsel = __popcll(valid);
@@ -154,22 +121,20 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 
   Frag kf[4];                 // A fragments of S^T = K Q^T, rows in perm_key order
   bf16x8 vf[2][D / 16];       // A fragments of O^T = V^T P^T: [key half][value column tile]
-  // rows past the end of the sequence are clamped to the last key: their logits are masked
+  // keys past the end of the sequence are zero in the packed blocks; their logits are masked
   auto load_k = [&](int leaf) {
-    const int64_t first = (int64_t)leaf * kLeaf;
+    const bf16x8* blk = kpack + (int64_t)leaf * (kLeaf * D / 8) + lane;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int64_t key = min(first + perm_key(mt, col), (int64_t)a.n - 1);
-      kf[mt].load(kbase + key * a.k_st, g);
-    }
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) kf[mt].v[s] = blk[(mt * (D / 32) + s) * 64];
   };
   auto load_v = [&](int leaf) {
-    const __bf16* blk = vtbase + (int64_t)leaf * D * kLeaf;
+    const bf16x8* blk = vpack + (int64_t)leaf * (kLeaf * D / 8) + lane;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        vf[kb][dt] = *reinterpret_cast<const bf16x8*>(blk + (16 * dt + col) * kLeaf + 32 * kb + 8 * g);
+      for (int dt = 0; dt < D / 16; ++dt) vf[kb][dt] = blk[(kb * (D / 16) + dt) * 64];
   };
 
   floatx4 o[D / 16];
@@ -321,9 +286,12 @@ template <typename TO, int D>
 hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
   if (a.bf16) {
-    hipLaunchKernelGGL((v_transpose_kernel<D>), dim3(ceil_div(a.n, kLeaf), a.batch * a.n_kv_heads), dim3(256), 0,
-                       s, a);
-    hipError_t e = hipGetLastError();
+    PackArgs p;
+    p.k = a.k; p.k_sb = a.k_sb; p.k_st = a.k_st; p.k_sh = a.k_sh;
+    p.v = a.v; p.v_sb = a.v_sb; p.v_st = a.v_st; p.v_sh = a.v_sh;
+    p.kpack = a.kpack; p.vpack = a.vpack;
+    p.batch = a.batch; p.n_kv_heads = a.n_kv_heads; p.head_dim = D; p.n = a.n;
+    hipError_t e = launch_pack(p, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, a);
   } else {

@@ -78,12 +78,38 @@ struct AttnArgs {
   void* o;
   int64_t o_sb, o_st, o_sh;
   float* row_lse;        // optional [B][Hq][N]
-  __bf16* vt;            // bf16 inputs: workspace for V^T blocks [B*Hkv][M1][d][64]
+  bf16x8* kpack;         // bf16 inputs: packed K blocks (see PackArgs), workspace
+  bf16x8* vpack;         // bf16 inputs: packed V blocks, workspace
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
   bool bf16;             // element type of q, k, v
   bool out_bf16;         // element type of o
 };
+
+// Packed 64-key blocks for bf16 K and V: every MFMA fragment of a block is one contiguous
+// 1 KB run in lane order (lane l = 16 g + col holds 16 bytes), so a fragment load reads whole
+// cache lines.  Block j of (b, kvh) occupies 64 d / 8 sixteen-byte pieces at
+// ((b * Hkv + kvh) * M1 + j) * 8 d.
+//   K piece (mt, s), mt < 4, s < d / 32, at (mt * d / 32 + s) * 64 + l: elements
+//     [32 s + 8 g, +8) of key 64 j + perm_key(mt, col).
+//   V piece (kb, dt), kb < 2, dt < d / 16, at (kb * d / 16 + dt) * 64 + l: column
+//     16 dt + col of keys 64 j + 32 kb + 8 g + i, i < 8.
+// Keys at or past n are zero.
+struct PackArgs {
+  const void* k;
+  int64_t k_sb, k_st, k_sh;
+  const void* v;            // may be null: K only
+  int64_t v_sb, v_st, v_sh;
+  bf16x8* kpack;
+  bf16x8* vpack;
+  int batch, n_kv_heads, head_dim, n;
+};
+
+// Key order inside a packed K block: M-tile mt = 2 kb + h, row m holds key
+// 32 kb + 8 (m / 4) + 4 h + m % 4.  In an S^T = K Q^T result lane group g of tiles (2 kb, 2 kb + 1)
+// then owns keys 32 kb + 8 g + 0..7, which is exactly the k-slice that the lane supplies to the
+// P V product of key half kb.
+__host__ __device__ inline int perm_key(int mt, int m) { return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3); }
 
 struct DecodeArgs {
   const void* q;            // [B][Hq][d]
@@ -108,6 +134,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // bf16 inputs: fills a.split from a.pyr for `rows` summary rows (B*Hkv*nodes).
 hipError_t launch_split_summaries(const RouteArgs& a, int64_t rows, hipStream_t s);

@@ -180,11 +180,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         const float s1 = __shfl(pair_score[1], src, 64);
         if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
       }
+      // exact rank among the candidates; lane j's values are read into scalar registers
       int rank = 0;
       for (int j = 0; j < span; ++j) {
-        const float uj = __shfl(u, j, 64);
-        const int cj = __shfl(cand, j, 64);
-        rank += (cj >= 0) && (uj > u || (uj == u && cj < cand));
+        const float uj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), j));
+        const int cj = __builtin_amdgcn_readlane(cand, j);
+        rank += (int)((cj >= 0) & ((uj > u) | ((uj == u) & (cj < cand))));
       }
       keep = cand >= 0 && rank < a.top_k;
     }

@@ -142,9 +142,10 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
                                int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes needed by pisa_sparse_attn_fwd for cfg: bf16 inputs stage V as
- * transposed 64-key blocks (B * H_kv * ceil(N / 64) * 64 * d * 2 bytes); fp32
- * inputs need none (0). */
+/* Workspace bytes needed by pisa_sparse_attn_fwd for cfg: bf16 inputs stage K and
+ * V as packed 64-key blocks, each fragment of the attention products one
+ * contiguous run (2 * B * H_kv * ceil(N / 64) * 64 * d * 2 bytes, each half
+ * rounded up to 256 bytes); fp32 inputs need none (0). */
 size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
 
 /*
