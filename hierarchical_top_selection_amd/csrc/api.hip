@@ -47,6 +47,16 @@ Levels make_levels(int n, int capacity) {
   return lv;
 }
 
+// Split-summary pair blocks of the levels of `lv`: offsets per level and the total.
+int64_t split_pairs(const Levels& lv, int64_t* pair_off) {
+  int64_t off = 0;
+  for (int l = 0; l < lv.count; ++l) {
+    if (pair_off) pair_off[l] = off;
+    off += (lv.size[l] + 1) / 2;
+  }
+  return off;
+}
+
 pisa_status check_cfg(const pisa_cfg* c) {
   if (!c) return PISA_ERR_INVALID_ARG;
   if (c->batch < 1 || c->seq_len < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->top_k < 1)
@@ -79,7 +89,7 @@ pisa_status hip_status(hipError_t e) {
 }
 
 struct SelectWorkspace {
-  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, total;
+  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, kpack, qpack, total;
   int n_windows, item_cap;
 };
 
@@ -100,9 +110,15 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   w.items = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
   w.n_items = align256(w.items + (size_t)bh * w.n_windows * w.item_cap * 8);
   w.split = align256(w.n_items + (size_t)bh * w.n_windows * 4);
-  // bf16 inputs: split summaries for routing, 4 bytes per pyramid element
-  const size_t split_bytes = c->dtype == PISA_BF16 ? (size_t)bh * make_levels(c->seq_len, c->seq_len).nodes * c->head_dim * 4 : 0;
-  w.total = align256(w.split + split_bytes);
+  // bf16 inputs: split summaries for routing (4 bytes per pyramid element), packed K
+  // blocks and packed query groups for the leaf scores
+  const bool bf16 = c->dtype == PISA_BF16;
+  const size_t split_bytes = bf16 ? (size_t)bh * split_pairs(make_levels(c->seq_len, c->seq_len), nullptr) * c->head_dim * 8 : 0;
+  const size_t kpack_bytes = bf16 ? (size_t)bh * m1 * pisa::kLeaf * c->head_dim * 2 : 0;
+  const size_t qpack_bytes = bf16 ? (size_t)bh * c->seq_len * c->n_q_heads / c->n_kv_heads * c->head_dim * 2 : 0;
+  w.kpack = align256(w.split + split_bytes);
+  w.qpack = align256(w.kpack + kpack_bytes);
+  w.total = align256(w.qpack + qpack_bytes);
   return w;
 }
 
@@ -186,8 +202,8 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16;
   r.lv = make_levels(N, N);
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
-  if (bf16 && (st = hip_status(pisa::launch_split_summaries(r, (int64_t)cfg->batch * cfg->n_kv_heads * r.lv.nodes, s))) != PISA_OK)
-    return st;
+  r.pairs = split_pairs(r.lv, r.pair_off);
+  if (bf16 && (st = hip_status(pisa::launch_split_summaries(r, s))) != PISA_OK) return st;
   if ((st = hip_status(pisa::launch_route(r, s))) != PISA_OK) return st;
 
   pisa::ClusterArgs c;
@@ -197,6 +213,22 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   c.items = items; c.n_items = n_items; c.item_cap = w.item_cap;
   if ((st = hip_status(pisa::launch_cluster(c, s))) != PISA_OK) return st;
 
+  pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
+  pisa::bf16x8* qpack = reinterpret_cast<pisa::bf16x8*>(base + w.qpack);
+  if (bf16) {
+    pisa::PackArgs p;
+    p.k = k.ptr; p.k_sb = k.stride_b; p.k_st = k.stride_t; p.k_sh = k.stride_h;
+    p.v = nullptr; p.v_sb = p.v_st = p.v_sh = 0;
+    p.kpack = kpack; p.vpack = nullptr;
+    p.batch = cfg->batch; p.n_kv_heads = cfg->n_kv_heads; p.head_dim = cfg->head_dim; p.n = N;
+    if ((st = hip_status(pisa::launch_pack(p, s))) != PISA_OK) return st;
+    pisa::QPackArgs qp;
+    qp.q = q.ptr; qp.q_sb = q.stride_b; qp.q_st = q.stride_t; qp.q_sh = q.stride_h;
+    qp.qpack = qpack;
+    qp.batch = cfg->batch; qp.n_kv_heads = cfg->n_kv_heads; qp.group = G; qp.head_dim = cfg->head_dim; qp.n = N;
+    if ((st = hip_status(pisa::launch_pack_queries(qp, s))) != PISA_OK) return st;
+  }
+
   pisa::LeafArgs l;
   l.q = q.ptr; l.q_sb = q.stride_b; l.q_st = q.stride_t; l.q_sh = q.stride_h;
   l.k = k.ptr; l.k_sb = k.stride_b; l.k_st = k.stride_t; l.k_sh = k.stride_h;
@@ -205,6 +237,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   l.n = N; l.width = width; l.n_leaves = m1; l.window = kWindow; l.n_windows = w.n_windows;
   l.items = items; l.n_items = n_items; l.item_cap = w.item_cap;
   l.scale = scale; l.bf16 = bf16;
+  l.kpack = kpack; l.qpack = qpack;
   if ((st = hip_status(pisa::launch_leaf_lse(l, s))) != PISA_OK) return st;
 
   pisa::TopkArgs t;

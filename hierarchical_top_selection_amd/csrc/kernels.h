@@ -23,7 +23,13 @@ struct RouteArgs {
   const void* q;
   int64_t q_sb, q_st, q_sh;
   const float* pyr;
-  uint16_t* split;        // bf16 inputs: [B*Hkv][nodes][2 d] summaries as bf16 high parts, then f16 remainders
+  // bf16 inputs: split summaries (bf16 high part, f16 remainder scaled by 2^10) by child
+  // pairs: nodes 2p, 2p + 1 of a level form a block of 8 d bytes at pair_off[level - 1] + p
+  // (per b * Hkv: `pairs` blocks).  Line (plane, s), plane 0 = high / 1 = remainder, s < d / 32,
+  // is 128 bytes: elements [32 s, 32 s + 32) of node 2p, then of node 2p + 1.
+  uint16_t* split;
+  int64_t pair_off[kMaxLevels];
+  int64_t pairs;
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
@@ -54,6 +60,8 @@ struct LeafArgs {
   const int2* items;
   const int32_t* n_items;
   float* leaf_u;         // [B*Hkv][N][2K]
+  const bf16x8* kpack;   // bf16 inputs: packed K blocks (PackArgs layout)
+  const bf16x8* qpack;   // bf16 inputs: packed query groups (QPackArgs layout)
   int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows, item_cap;
   float scale;
   bool bf16;
@@ -105,6 +113,17 @@ struct PackArgs {
   int batch, n_kv_heads, head_dim, n;
 };
 
+// Packed bf16 query groups: the G heads of (b, kvh) at token t occupy G d / 8 sixteen-byte
+// pieces at ((b * Hkv + kvh) * N + t) * G d / 8; piece (s, g, col), s < d / 32, g < 4, col < G,
+// at (4 s + g) * G + col holds elements [32 s + 8 g, +8) of head kvh * G + col, so the MFMA
+// B fragment of a query (lane 16 g + col) is one contiguous run.
+struct QPackArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  bf16x8* qpack;
+  int batch, n_kv_heads, group, head_dim, n;
+};
+
 // Key order inside a packed K block: M-tile mt = 2 kb + h, row m holds key
 // 32 kb + 8 (m / 4) + 4 h + m % 4.  In an S^T = K Q^T result lane group g of tiles (2 kb, 2 kb + 1)
 // then owns keys 32 kb + 8 g + 0..7, which is exactly the k-slice that the lane supplies to the
@@ -135,9 +154,10 @@ struct DecodeArgs {
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_pack_queries(const QPackArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-// bf16 inputs: fills a.split from a.pyr for `rows` summary rows (B*Hkv*nodes).
-hipError_t launch_split_summaries(const RouteArgs& a, int64_t rows, hipStream_t s);
+// bf16 inputs: fills a.split from a.pyr.
+hipError_t launch_split_summaries(const RouteArgs& a, hipStream_t s);
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);

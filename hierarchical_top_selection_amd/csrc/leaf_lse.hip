@@ -5,7 +5,9 @@
 // Leaf-major: a wave walks a few work items (each one leaf of one token window,
 // at most kPairsPerItem queries).  The leaf's 64 keys are loaded once into MFMA
 // A fragments held in registers (bf16: 64 VGPRs at d = 128) and reused by every
-// query of the item; each query streams in only its G head rows (the B tile).  The product is kept transposed, S^T = K Q^T
+// query of the item; each query streams in only its G head rows (the B tile).
+// bf16 inputs read both from packed copies (K blocks with keys in perm_key order,
+// query groups; pack.hip) so every fragment load is one contiguous run.  The product is kept transposed, S^T = K Q^T
 // (keys on rows, heads on columns), so a lane owns 16 keys of one head: the
 // per-head max and sum over the 64 keys are in-lane plus two cross-group
 // shuffles, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
@@ -33,15 +35,18 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     acc[mt] = mma(kf[mt], qf, acc[mt]);
   }
-  // acc[mt][r]: key (start + 16 mt + 4 g + r) against head column col.  Keys past
-  // min(t, n - 1) are masked; `last` is n - 1 - start capped at 63.
+  // acc[mt][r]: key start + key_offset(mt, 4 g + r) against head column col (packed bf16
+  // blocks hold keys in perm_key order, fp32 keys are in order).  Keys past min(t, n - 1)
+  // are masked; `last` is n - 1 - start capped at 63.
   const int lim = min(t - start, last);
   if (lim < kLeaf - 1) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * mt + 4 * g + r > lim) acc[mt][r] = kNegInf;
+      for (int r = 0; r < 4; ++r) {
+        const int off = sizeof(T) == 2 ? 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + r : 16 * mt + 4 * g + r;
+        if (off > lim) acc[mt][r] = kNegInf;
+      }
   }
   float m = kNegInf;
 #pragma unroll
@@ -97,8 +102,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
     const int np = rec.y >> 20, p0 = rec.y & 0xfffff;
     return lane < np ? pairs[p0 + lane] : 0;
   };
+  const int64_t qp_token = (int64_t)a.group * D / 8;                  // packed query pieces per token
+  const bf16x8* qpack = a.qpack + (int64_t)bh * a.n * qp_token + g * a.group + col;
   auto load_q = [&](Frag& f, int packed) {
-    if (head_ok) f.load(qbase + (int64_t)(packed >> 6) * a.q_st, g); else f.zero();
+    if (!head_ok) {
+      f.zero();
+    } else if constexpr (sizeof(T) == 2) {
+      const bf16x8* p = qpack + (int64_t)(packed >> 6) * qp_token;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) f.v[s] = p[4 * s * a.group];
+    } else {
+      f.load(qbase + (int64_t)(packed >> 6) * a.q_st, g);
+    }
   };
 
   int2 rec = items[it0];
@@ -112,10 +127,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
   for (int it = it0; it < it_end; ++it) {
     const int leaf = rec.x, np = rec.y >> 20;
     const int2 rec_nn = it + 2 < it_end ? items[it + 2] : make_int2(-1, 0);
-    if (leaf != cur_leaf) {                            // rows past the end are clamped, then masked
-      const int64_t first = (int64_t)leaf * kLeaf;
+    if (leaf != cur_leaf) {                            // rows past the end are zero or clamped, then masked
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8* blk = a.kpack + ((int64_t)bh * a.n_leaves + leaf) * (kLeaf * D / 8) + lane;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int s = 0; s < D / 32; ++s) kf[mt].v[s] = blk[(mt * (D / 32) + s) * 64];
+      } else {
+        const int64_t first = (int64_t)leaf * kLeaf;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+      }
       cur_leaf = leaf;
     }
     const int start = leaf * kLeaf;

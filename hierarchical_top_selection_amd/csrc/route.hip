@@ -30,17 +30,19 @@ namespace pisa {
 // Query operands (B tile columns) and summary tiles (A tile rows) of one precision.
 template <typename T, int D> struct RouteOps;
 
+// Tile::load(a, rows, li, child, g): row `child` of pyramid level li + 1 for lane group g.
 template <int D> struct RouteOps<float, D> {         // fp32 summaries, fp32 MFMA
   typedef float Row;
-  static constexpr int kRowElems = D;
   struct Q { FragF32<D> f; };
   struct Tile {
     FragF32<D> f;
-    __device__ inline void load(const Row* rows, int64_t node, int g) { f.load(rows + node * kRowElems, g); }
+    __device__ inline void load(const RouteArgs& a, const Row* rows, int li, int child, int g) {
+      f.load(rows + (a.lv.offset[li] + child) * D, g);
+    }
   };
   __device__ static inline void load_q(Q& q, const float* row, int g) { q.f.load(row, g); }
   __device__ static inline void zero_q(Q& q) { q.f.zero(); }
-  __device__ static inline const Row* rows(const RouteArgs& a) { return a.pyr; }
+  __device__ static inline const Row* rows(const RouteArgs& a, int bh) { return a.pyr + (int64_t)bh * a.lv.nodes * D; }
   __device__ static inline floatx4 dot(const Tile& t, const Q& q) {
     return mma(t.f, q.f, floatx4{0.f, 0.f, 0.f, 0.f});
   }
@@ -48,15 +50,19 @@ template <int D> struct RouteOps<float, D> {         // fp32 summaries, fp32 MFM
 
 template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 remainder
   typedef uint16_t Row;
-  static constexpr int kRowElems = 2 * D;
   struct Q { FragBF16<D> h; FragF16<D> l; };
   struct Tile {
     FragBF16<D> h;
     FragF16<D> l;
-    __device__ inline void load(const Row* rows, int64_t node, int g) {
-      const Row* r = rows + node * kRowElems;
-      h.load(reinterpret_cast<const __bf16*>(r), g);
-      l.load(reinterpret_cast<const _Float16*>(r + D), g);
+    // tile rows 2 i, 2 i + 1 are the two children of one candidate, so each fragment
+    // load covers whole 128-byte lines of the pair blocks
+    __device__ inline void load(const RouteArgs& a, const Row* rows, int li, int child, int g) {
+      const Row* r = rows + (a.pair_off[li] + (child >> 1)) * (4 * D) + 32 * (child & 1) + 8 * g;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        h.v[s] = *reinterpret_cast<const bf16x8*>(r + 64 * s);
+        l.v[s] = *reinterpret_cast<const f16x8*>(r + 64 * (D / 32 + s));
+      }
     }
   };
   // bf16 values are exact in f16 up to its range; larger ones saturate
@@ -74,7 +80,7 @@ template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 rem
 #pragma unroll
       for (int j = 0; j < 8; ++j) q.l.v[s][j] = (_Float16)0.f;
   }
-  __device__ static inline const Row* rows(const RouteArgs& a) { return a.split; }
+  __device__ static inline const Row* rows(const RouteArgs& a, int bh) { return a.split + (int64_t)bh * a.pairs * (4 * D); }
   __device__ static inline floatx4 dot(const Tile& t, const Q& q) {
     const floatx4 hi = mma(t.h, q.h, floatx4{0.f, 0.f, 0.f, 0.f});
     const floatx4 lo = mma(t.l, q.l, floatx4{0.f, 0.f, 0.f, 0.f});
@@ -82,28 +88,41 @@ template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 rem
   }
 };
 
-// Row r of the split layout: [bf16(x) for the d elements][f16((x - bf16(x)) 2^10)], each
-// conversion to nearest, the remainder clamped to the f16 range.  One thread per 8 elements.
+// Fills the pair blocks of the split layout (RouteArgs): one thread per 16-byte piece q of a
+// block, q = 8 line + 4 c + g with elements [32 s + 8 g, +8) of node 2p + c (zero past the
+// level's end).  hi = bf16(x) to nearest; the remainder x - hi is exact in fp32, is scaled by
+// 2^10 and rounded to the nearest f16 after clamping to its range.
 template <int D>
-__global__ __launch_bounds__(256) void split_summaries_kernel(const float* pyr, uint16_t* out, int64_t rows) {
+__global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
+  constexpr int kPieces = D / 2;                      // 16-byte pieces per pair block
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = e / (D / 8);
-  const int c8 = (int)(e % (D / 8));
-  if (row >= rows) return;
-  const float4 a = *reinterpret_cast<const float4*>(pyr + row * D + 8 * c8);
-  const float4 b = *reinterpret_cast<const float4*>(pyr + row * D + 8 * c8 + 4);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  bf16x8 hi;
-  f16x8 lo;
+  const int64_t blk = e / kPieces;                    // bh * pairs + pair
+  if (blk >= (int64_t)a.batch * a.n_kv_heads * a.pairs) return;
+  const int q = (int)(e % kPieces);
+  const int bh = (int)(blk / a.pairs);
+  const int64_t pr = blk % a.pairs;
+  int li = 0;
+  while (li + 1 < a.lv.count && pr >= a.pair_off[li + 1]) ++li;
+  const int64_t node = 2 * (pr - a.pair_off[li]) + ((q >> 2) & 1);
+  const int line = q >> 3, g = q & 3;
+  const int plane = line / (D / 32), s = line % (D / 32);
+  uint4 out = make_uint4(0u, 0u, 0u, 0u);
+  if (node < a.lv.size[li]) {
+    const float* src = a.pyr + ((int64_t)bh * a.lv.nodes + a.lv.offset[li] + node) * D + 32 * s + 8 * g;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    bf16x8 hi;
+    f16x8 lo;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    hi[j] = (__bf16)x[j];
-    const float r = (x[j] - (float)hi[j]) * 1024.f;  // exact: x and hi agree to 8 bits
-    lo[j] = (_Float16)fminf(fmaxf(r, -65504.f), 65504.f);
+    for (int j = 0; j < 8; ++j) {
+      hi[j] = (__bf16)x[j];
+      const float r = (x[j] - (float)hi[j]) * 1024.f;
+      lo[j] = (_Float16)fminf(fmaxf(r, -65504.f), 65504.f);
+    }
+    out = plane == 0 ? __builtin_bit_cast(uint4, hi) : __builtin_bit_cast(uint4, lo);
   }
-  uint16_t* dst = out + row * 2 * D;
-  *reinterpret_cast<bf16x8*>(dst + 8 * c8) = hi;
-  *reinterpret_cast<f16x8*>(dst + D + 8 * c8) = lo;
+  *reinterpret_cast<uint4*>(a.split + e * 8) = out;
 }
 
 // ----------------------------------------------------------------------------- routing
@@ -127,14 +146,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   } else {
     Ops::zero_q(qf);
   }
-  const typename Ops::Row* rows = Ops::rows(a) + (int64_t)bh * a.lv.nodes * Ops::kRowElems;
+  const typename Ops::Row* rows = Ops::rows(a, bh);
 
   int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
   for (int level = a.lv.count; level >= 2; --level) {
     const uint64_t valid = __ballot(cand >= 0);
     const int n_valid = __popcll(valid);
     const int child_size = a.lv.size[level - 2];
-    const int64_t child_off = a.lv.offset[level - 2];
     bool keep = cand >= 0;
     if (n_valid > a.top_k) {
       const int span = 64 - __clzll(valid);            // highest occupied lane + 1
@@ -152,14 +170,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       bool ok_n;
       int child_n = child_of(0, ok_n);
       typename Ops::Tile kf_n;
-      kf_n.load(rows, child_off + child_n, g);
+      kf_n.load(a, rows, level - 2, child_n, g);
       for (int nt = 0; nt < tiles; ++nt) {
         const typename Ops::Tile kf = kf_n;
         // validity of the children this lane holds results for: rows 4g .. 4g+3 of the tile
         const uint64_t okmask = __ballot(ok_n);
         if (nt + 1 < tiles) {                          // next tile's rows in flight during this one
           child_n = child_of(nt + 1, ok_n);
-          kf_n.load(rows, child_off + child_n, g);
+          kf_n.load(a, rows, level - 2, child_n, g);
         }
         // S^T tile: rows = 16 children, columns = heads; lane (g, col) gets children 4g + i of head col
         const floatx4 acc = Ops::dot(kf, qf);
@@ -208,13 +226,13 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_split_summaries(const RouteArgs& a, int64_t rows, hipStream_t s) {
-  const int64_t threads = rows * (a.head_dim / 8);
+hipError_t launch_split_summaries(const RouteArgs& a, hipStream_t s) {
+  const int64_t threads = (int64_t)a.batch * a.n_kv_heads * a.pairs * (a.head_dim / 2);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(split_summaries_kernel<64>, dim3(blocks), dim3(256), 0, s, a.pyr, a.split, rows);
+    hipLaunchKernelGGL(split_summaries_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(split_summaries_kernel<128>, dim3(blocks), dim3(256), 0, s, a.pyr, a.split, rows);
+    hipLaunchKernelGGL(split_summaries_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -134,8 +134,9 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  *   sel     : int32 [B][H_kv][N][K] output, ascending, -1 padded
  *   sel_u   : optional float32 [B][H_kv][N][K] output (NULL to skip): the leaf
  *             score u of each selected block, -inf on padding
- *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes (it
- *             also holds the split summaries of bf16 inputs); its first
+ *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes (for
+ *             bf16 inputs it also holds the split summaries and packed copies
+ *             of K and Q, about the size of q plus k); its first
  *             B*H_kv*N*2K int32 hold the leaf candidates of each token (-1
  *             padded) after the call
  */
