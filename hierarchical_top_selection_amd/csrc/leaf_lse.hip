@@ -64,12 +64,8 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
   s = wave_add_xor(s, 16);
   s = wave_add_xor(s, 32);
   // natural-log LSE of this head: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
-  float u = head_ok ? (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f : 0.f;
-  u = wave_add_xor(u, 1);
-  u = wave_add_xor(u, 2);
-  u = wave_add_xor(u, 4);
-  u = wave_add_xor(u, 8);
-  if (lane == 0) uout[(int64_t)t * a.width + slot] = u;
+  const float u = row_sum_to_last(head_ok ? (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f : 0.f);
+  if (lane == 15) uout[(int64_t)t * a.width + slot] = u;   // the group's head sum (row 0)
 }
 
 // Each wave walks kItemsPerWave consecutive items of one window.  The next item's
@@ -123,7 +119,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
   Frag kf[4];
   int cur_leaf = -1;
   Frag q0, q1;
-  load_q(q0, __shfl(pr, 0, 64));
+  load_q(q0, __builtin_amdgcn_readfirstlane(pr));
   for (int it = it0; it < it_end; ++it) {
     const int leaf = rec.x, np = rec.y >> 20;
     const int2 rec_nn = it + 2 < it_end ? items[it + 2] : make_int2(-1, 0);
@@ -147,9 +143,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
       // rows of the following query (this item's next, or the next item's first)
       const bool in_item = i + 1 < np;
       const bool have_next = in_item || it + 1 < it_end;
-      const int nxt = __shfl(in_item ? pr : pr_n, in_item ? i + 1 : 0, 64);
+      // lane broadcasts of the uniform pair index: scalar reads, no LDS round trip
+      const int nxt = in_item ? __builtin_amdgcn_readlane(pr, i + 1) : __builtin_amdgcn_readfirstlane(pr_n);
       if (have_next) load_q(q1, nxt);
-      leaf_pair<T, D>(kf, q0, __shfl(pr, i, 64), a, start, last, c2, head_ok, g, lane, uout);
+      leaf_pair<T, D>(kf, q0, __builtin_amdgcn_readlane(pr, i), a, start, last, c2, head_ok, g, lane, uout);
       q0 = q1;
     }
     if (it + 1 < it_end) {
