@@ -11,9 +11,11 @@ resident in HBM.  Prints ONE JSON line (see the design notes for the fields).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -156,6 +158,74 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
             "attn_ms": attn_ms, "tokens_per_s": B * N / (wall_ms / 1e3), "attn_flops": flops}
 
 
+def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
+    """Decode throughput: `decode_steps` steps of every sequence after a prebuilt context.
+
+    The 2 x 17 GB bf16 caches are drawn on the device with a seeded torch generator
+    (N(0, 1), like the workload's recipe; drawing them on the host would take minutes).
+    One untimed pass of all steps runs first; the pyramid is then rebuilt for the
+    context length, so the timed pass starts from the same state.
+    """
+    import torch
+
+    from hierarchical_top_selection_amd import binding
+
+    B, n0, Hq, Hkv, d, K, S = w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.top_k, w.decode_steps
+    cap = n0 + S
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(w.seed)
+    kc = torch.randn((B, cap, Hkv, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
+    vc = torch.randn((B, cap, Hkv, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
+    qs = torch.randn((S, B, Hq, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
+    ks = kc[:, n0:].permute(1, 0, 2, 3).contiguous()          # the appended tokens, [S, B, Hkv, d]
+    vs = vc[:, n0:].permute(1, 0, 2, 3).contiguous()
+    pyr = torch.empty((B, Hkv, binding.pyramid_nodes(cap), d), dtype=torch.float32, device="cuda:0")
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda:0")
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda:0")
+
+    def one_pass(ev=None):
+        binding.build_pyramid(kc, n=n0, capacity=cap, out=pyr)
+        if ev is not None:
+            ev[0].record()
+        for s in range(S):
+            binding.decode_step(qs[s], ks[s], vs[s], kc, vc, pyr, n0 + s, K, out=o, sel_out=sel)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup_passes):
+        one_pass()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    one_pass(ev)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[1])
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": B * S / (total_ms * 1e-3), "ms_per_step": total_ms / S, "steps": S, "batch": B,
+            "context": n0, "data": "synthetic: device-drawn N(0,1), seeded torch generator"}
+
+
+# Counter summary of the dominant kernel (committed under profiles/).  Its traffic figure is
+# reported only while the kernel's sources are the ones the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_n262144_traffic.md")
+TRAFFIC_SOURCES = ("attention.hip", "kernels.h", "pisa_device.h")
+
+
+def attention_traffic(workload: str):
+    """HBM-side bytes per attention launch (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
+    if workload != "prefill_n262144" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = dict(re.findall(r"^(source_sha256|fetch_bytes_per_launch|write_bytes_per_launch): (\S+)\s*$",
+                             open(TRAFFIC_FILE).read(), re.M))
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "hierarchical_top_selection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if len(fields) != 3 or h.hexdigest() != fields["source_sha256"]:
+        return None
+    return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +235,7 @@ def main() -> int:
     ap.add_argument("--also", default="prefill_n32768", help="comma-separated extra workloads to report")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode timing record")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times), for scaling HBM byte counters")
     args = ap.parse_args()
@@ -195,6 +266,8 @@ def main() -> int:
         r = run_workload(W.WORKLOADS[name], args.steps, args.warmup)
         extra[name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                        "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"]}
+    if not args.no_decode:
+        extra["decode_b64_ctx131072"] = run_decode(W.WORKLOADS["decode_b64_ctx131072"])
     attn_tflops = main_run["attn_flops"] / (main_run["attn_ms"] * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     line = {
@@ -216,8 +289,10 @@ def main() -> int:
         "pyramid_ms": main_run["pyramid_ms"],
         "select_ms": main_run["select_ms"],
         "attn_ms": main_run["attn_ms"],
-        "roofline": {"kernel": "attention_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None},
+        # attention_bf16_kernel, timed with the block packing that sparse_attn_fwd runs before it
+        # (about 0.4% of the call); flops count valid keys only
+        "roofline": {"kernel": "attention_bf16_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": attention_traffic(w.name)},
         "cpu_baseline": cpu,
         "also": extra,
     }
