@@ -5,12 +5,9 @@
 //
 // The update runs one workgroup per (b, kvh) with one thread per column and the
 // same pooling functions as the prefill build, so the pyramid stays
-// bit-identical to a rebuild.  The fused kernel is one workgroup per (b, kvh):
-// levels are serial, candidates parallel; the leaf logits of every candidate
-// leaf are staged in LDS and reused by the attention of the selected leaves, so
-// selected keys are read from HBM once.  Decode is HBM-bound, so it uses fp32
-// FMA on the VALU (G is a template parameter to keep the head accumulators in
-// registers).
+// bit-identical to a rebuild.  The fused kernel is one multi-wave workgroup per
+// (b, kvh): levels are serial, the work inside each level, the candidate leaves
+// and the attended blocks are spread over the waves (see the kernel's comment).
 #include "kernels.h"
 #include "pyramid_dev.h"
 
@@ -48,206 +45,187 @@ __global__ __launch_bounds__(128) void decode_update_kernel(DecodeArgs a) {
   }
 }
 
-// LDS carve-up of the fused kernel (floats unless noted).
+// ----------------------------------------------------------------------------- fused route + attend
+// One workgroup of kDecodeWaves waves per (b, kvh).  Every phase spreads its work over the waves:
+//  * routing, level by level from the root: the candidates' children are scored 16 at a time as the
+//    rows of an S^T = (children) Q^T MFMA tile (fp32 summaries, v_mfma_f32_16x16x4_f32), one tile per
+//    wave; a candidate's two children sit in the same lane, so its per-head LSE is in-lane and the
+//    head sum a DPP row reduction; wave 0 ranks (score descending, index ascending) and expands;
+//  * leaf scoring: one candidate leaf per wave, S^T over its 64 raw keys on the input type's MFMA;
+//    the logits (base-2 units) are staged in LDS and reused by the attention, so the selected keys
+//    are read from HBM once;
+//  * attention: softmax statistics per head over the selected leaves' staged logits, then P V with
+//    one selected block per wave, 16 value rows in flight at a time, and a fixed-order sum of the
+//    per-wave partial outputs.
+constexpr int kDecodeWaves = 8;
+
+// LDS carve-up of the fused kernel (4-byte words).
 struct DecodeLds {
-  int qs, zc, zl, part, ints;
+  int zl, part, us, hstat, ints;
   size_t bytes;
   __host__ __device__ DecodeLds(int G, int width, int D) {
-    qs = 0;                          // G * D query rows
-    zc = qs + G * D;                 // 128 child slots * G logits
-    zl = zc + 128 * G;               // width * 64 * G leaf logits, then probabilities
-    part = zl + width * 64 * G;      // 4 waves * G * D partial outputs
-    ints = part + 4 * G * D;         // int scratch: 6 * 64 + 8
-    bytes = (size_t)(ints + 6 * 64 + 8) * 4;
+    zl = 0;                                   // width * 64 * G staged leaf logits, then probabilities
+    part = zl + width * kLeaf * G;            // kDecodeWaves * G * D partial outputs
+    us = part + kDecodeWaves * G * D;         // 64 candidate scores
+    hstat = us + 64;                          // per-head max and 1 / sum
+    ints = hstat + 2 * G;                     // cand[64], keep[64], selv[64], sels[64], misc[4]
+    bytes = (size_t)(ints + 4 * 64 + 4) * 4;
   }
 };
 
+// Wave 0: keep candidates by exact rank (u descending, index ascending) or, when at most K
+// are valid, all of them.  Returns this lane's keep flag (lane i = slot i).
+__device__ inline bool decode_keep(const int* cand, const float* us, int nslots, int nvalid, int K, int lane) {
+  const int ci = lane < nslots ? cand[lane] : -1;
+  if (nvalid <= K) return ci >= 0;
+  const float ui = lane < nslots ? us[lane] : kNegInf;
+  int rank = 0;
+  for (int j = 0; j < nslots; ++j) {
+    const float uj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ui), j));
+    const int cj = __builtin_amdgcn_readlane(ci, j);
+    rank += (int)((cj >= 0) & ((uj > ui) | ((uj == ui) & (cj < ci))));
+  }
+  return ci >= 0 && rank < K;
+}
+
 template <typename T, typename TO, int D, int G>
-__global__ __launch_bounds__(256) void decode_fused_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(DecodeArgs a) {
+  typedef typename RawFrag<T, D>::type Frag;
   extern __shared__ __align__(16) float smem[];
   const int width = 2 * a.top_k, K = a.top_k;
   const DecodeLds L(G, width, D);
-  float* qs = smem + L.qs;
-  float* zc = smem + L.zc;
   float* zl = smem + L.zl;
   float* part = smem + L.part;
+  float* us = smem + L.us;
+  float* hstat = smem + L.hstat;
   int* cand = reinterpret_cast<int*>(smem + L.ints);
-  int* cand2 = cand + 64;
-  float* us = reinterpret_cast<float*>(cand2 + 64);
-  int* keep = reinterpret_cast<int*>(us + 64);
+  int* keep = cand + 64;
   int* selv = keep + 64;               // selected leaf ids, ascending
   int* sels = selv + 64;               // their candidate slots
   int* misc = sels + 64;               // [0] slots, [1] valid, [2] selected
-  float* hstat = zc;                   // per-head max and 1/sum, reused after routing
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
   const int bh = blockIdx.x;
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const int64_t t = a.n_ctx;           // query position: every stored key is valid
-  const T* qsrc = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)kvh * G * a.q_sh;
-  for (int e = tid; e < G * D; e += blockDim.x) qs[e] = to_f32(qsrc[(e / D) * a.q_sh + e % D]);
-  if (tid == 0) { cand[0] = 0; misc[0] = 1; misc[1] = 1; }
-  __syncthreads();
+  const int t = a.n_ctx;               // query position: every stored key is valid
+  const float c2 = a.scale * 1.4426950408889634f;   // logits in base-2 units
+  const bool head_ok = col < G;
+  const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)(kvh * G + (head_ok ? col : 0)) * a.q_sh;
   const float* pyr = a.pyr + (int64_t)bh * a.lv.nodes * D;
 
+  if (tid < 64) cand[tid] = tid == 0 ? 0 : -1;  // A^(L) = {root}
+  if (tid == 0) { misc[0] = 1; misc[1] = 1; }
+  __syncthreads();
+
+  // ---- routing, levels L .. 2
+  FragF32<D> qf;
+  if (head_ok) qf.load(qrow, g); else qf.zero();
   for (int level = a.lv.count; level >= 2; --level) {
     const int nslots = misc[0], nvalid = misc[1];
     const int child_size = a.lv.size[level - 2];
     const float* child_base = pyr + a.lv.offset[level - 2] * D;
     if (nvalid > K) {
-      for (int e = tid; e < 2 * nslots * G; e += blockDim.x) {
-        const int slot = e / G, h = e % G;
+      const int tiles = (2 * nslots + 15) / 16;
+      for (int nt = wave; nt < tiles; nt += kDecodeWaves) {
+        const int slot = 16 * nt + col;
         const int parent = cand[slot >> 1];
         const int child = 2 * parent + (slot & 1);
-        float z = kNegInf;
-        if (parent >= 0 && child < child_size) {
-          const float* row = child_base + (int64_t)child * D;
-          const float* qh = qs + h * D;
-          float acc = 0.f;
-          for (int c = 0; c < D; c += 4) {
-            const float4 r = *reinterpret_cast<const float4*>(row + c);
-            acc = fmaf(r.x, qh[c], acc);
-            acc = fmaf(r.y, qh[c + 1], acc);
-            acc = fmaf(r.z, qh[c + 2], acc);
-            acc = fmaf(r.w, qh[c + 3], acc);
-          }
-          z = acc * a.scale;
+        const bool ok = parent >= 0 && child < child_size;
+        FragF32<D> kf;
+        kf.load(child_base + (int64_t)(ok ? child : 0) * D, g);
+        const uint64_t okmask = __ballot(ok);
+        const floatx4 acc = mma(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                   // candidate 8 nt + 2 g + h: rows 4 g + 2 h, +1
+          const int r0 = 4 * g + 2 * h;
+          const float z0 = ((okmask >> r0) & 1) ? acc[2 * h] * c2 : kNegInf;
+          const float z1 = ((okmask >> (r0 + 1)) & 1) ? acc[2 * h + 1] * c2 : kNegInf;
+          const float m = fmaxf(z0, z1);
+          const float sc = m == kNegInf ? kNegInf : m + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(z0, z1) - m));
+          const float u = row_sum_to_last(head_ok ? sc : 0.f);
+          if (col == 15) us[8 * nt + 2 * g + h] = u;
         }
-        zc[slot * G + h] = z;
       }
-      __syncthreads();
-      for (int i = tid; i < nslots; i += blockDim.x) {
-        float u = kNegInf;
-        if (cand[i] >= 0) {
-          u = 0.f;
-          for (int h = 0; h < G; ++h) {
-            const float z0 = zc[(2 * i) * G + h], z1 = zc[(2 * i + 1) * G + h];
-            const float m = fmaxf(z0, z1);
-            u += m + logf(expf(z0 - m) + expf(z1 - m));
-          }
-        }
-        us[i] = u;
-      }
-      __syncthreads();
-      for (int i = tid; i < nslots; i += blockDim.x) {
-        const int ci = cand[i];
-        int rank = 0;
-        if (ci >= 0)
-          for (int j = 0; j < nslots; ++j) {
-            const int cj = cand[j];
-            rank += (cj >= 0) && (us[j] > us[i] || (us[j] == us[i] && cj < ci));
-          }
-        keep[i] = ci >= 0 && rank < K;
-      }
-    } else {
-      for (int i = tid; i < nslots; i += blockDim.x) keep[i] = cand[i] >= 0;
     }
     __syncthreads();
     if (wave == 0) {
-      const bool kp = lane < nslots && keep[lane];
-      const uint64_t km = __ballot(kp);
-      const int pos = __popcll(km & ((1ull << lane) - 1ull));
-      if (kp) {
-        const int parent = cand[lane];
-        cand2[2 * pos] = 2 * parent < child_size ? 2 * parent : -1;
-        cand2[2 * pos + 1] = 2 * parent + 1 < child_size ? 2 * parent + 1 : -1;
-      }
-      wave_lds_sync();
-      const int m2 = 2 * __popcll(km);
-      const int v = lane < m2 ? cand2[lane] : -1;
-      cand[lane] = v;
-      const int nv = __popcll(__ballot(v >= 0));
-      if (lane == 0) { misc[0] = m2; misc[1] = nv; }
+      const bool kp = decode_keep(cand, us, nslots, nvalid, K, lane);
+      const int ci = lane < nslots ? cand[lane] : -1;
+      const uint64_t kept = __ballot(kp);
+      const int m = __popcll(kept);
+      const int p = lane >> 1;
+      const int parent = __shfl(ci, nth_set_bit(kept, p < m ? p : 0), 64);
+      const int child = 2 * parent + (lane & 1);
+      const int nc = (p < m && child < child_size) ? child : -1;
+      cand[lane] = nc;
+      const int nv = __popcll(__ballot(nc >= 0));
+      if (lane == 0) { misc[0] = 2 * m; misc[1] = nv; }
     }
     __syncthreads();
   }
 
-  // leaf level: exact logits of every candidate leaf, staged for the attention
+  // ---- leaf level: exact logits of every candidate leaf over its raw keys <= t
   const int nslots = misc[0], nvalid = misc[1];
+  Frag qr;
+  if (head_ok) qr.load(qrow, g); else qr.zero();
   const T* kbase = reinterpret_cast<const T*>(a.k_cache) + b * a.kc_sb + kvh * a.kc_sh;
-  for (int e = tid; e < nslots * kLeaf; e += blockDim.x) {
-    const int slot = e / kLeaf, r = e % kLeaf;
+  for (int slot = wave; slot < nslots; slot += kDecodeWaves) {
     const int leaf = cand[slot];
-    const int64_t key = (int64_t)leaf * kLeaf + r;
-    float acc[G];
+    if (leaf < 0) continue;                             // wave-uniform
+    const int first = leaf * kLeaf;
+    floatx4 acc[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = kNegInf;
-    if (leaf >= 0 && key <= t) {
+    for (int mt = 0; mt < 4; ++mt) {                    // rows past t are clamped to t, then masked
+      Frag kf;
+      kf.load(kbase + (int64_t)min(first + 16 * mt + col, t) * a.kc_st, g);
+      acc[mt] = mma(kf, qr, floatx4{0.f, 0.f, 0.f, 0.f});
+    }
+    // acc[mt][r]: key first + 16 mt + 4 g + r, head col
+    float m = kNegInf;
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0.f;
-      const T* krow = kbase + key * a.kc_st;
-      for (int c = 0; c < D; c += 4) {
-        const float4 kk = load4(krow + c);
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float* qh = qs + h * D + c;
-          acc[h] = fmaf(kk.x, qh[0], acc[h]);
-          acc[h] = fmaf(kk.y, qh[1], acc[h]);
-          acc[h] = fmaf(kk.z, qh[2], acc[h]);
-          acc[h] = fmaf(kk.w, qh[3], acc[h]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * mt + 4 * g + r;
+        const float z = first + key <= t ? acc[mt][r] * c2 : kNegInf;
+        acc[mt][r] = z;
+        m = fmaxf(m, z);
+        if (head_ok) zl[(slot * kLeaf + key) * G + col] = z;
       }
+    m = wave_max_xor(m, 16);
+    m = wave_max_xor(m, 32);
+    float sum = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] *= a.scale;
-    }
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int h = 0; h < G; ++h) zl[(slot * kLeaf + r) * G + h] = acc[h];
-  }
-  __syncthreads();
-  if (nvalid > K) {
-    for (int i = tid; i < nslots; i += blockDim.x) {
-      float u = kNegInf;
-      if (cand[i] >= 0) {
-        u = 0.f;
-        for (int h = 0; h < G; ++h) {
-          float m = kNegInf;
-          for (int r = 0; r < kLeaf; ++r) m = fmaxf(m, zl[(i * kLeaf + r) * G + h]);
-          float s = 0.f;
-          for (int r = 0; r < kLeaf; ++r) s += expf(zl[(i * kLeaf + r) * G + h] - m);
-          u += m + logf(s);
-        }
-      }
-      us[i] = u;
-    }
-    __syncthreads();
-    for (int i = tid; i < nslots; i += blockDim.x) {
-      const int ci = cand[i];
-      int rank = 0;
-      if (ci >= 0)
-        for (int j = 0; j < nslots; ++j) {
-          const int cj = cand[j];
-          rank += (cj >= 0) && (us[j] > us[i] || (us[j] == us[i] && cj < ci));
-        }
-      keep[i] = ci >= 0 && rank < K;
-    }
-  } else {
-    for (int i = tid; i < nslots; i += blockDim.x) keep[i] = cand[i] >= 0;
+      for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(acc[mt][r] - m);   // key t is valid: m finite
+    sum = wave_add_xor(sum, 16);
+    sum = wave_add_xor(sum, 32);
+    const float u = row_sum_to_last(head_ok ? m + __builtin_amdgcn_logf(sum) : 0.f);
+    if (lane == 15) us[slot] = u;
   }
   __syncthreads();
   if (wave == 0) {
-    const bool kp = lane < nslots && keep[lane];
+    const bool kp = decode_keep(cand, us, nslots, nvalid, K, lane);
     const int c = kp ? cand[lane] : 0x7fffffff;
-    int pos = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int cj = __shfl(c, j, 64);
-      const bool kj = __shfl((int)kp, j, 64) != 0;
-      pos += kj && cj < c;
-    }
+    int pos = 0;                                        // ascending leaf order among the kept
+    for (int j = 0; j < 64; ++j) pos += __builtin_amdgcn_readlane(c, j) < c;
     if (kp) { selv[pos] = c; sels[pos] = lane; }
-    const int ns = __popcll(__ballot(kp));
+    const int ns = __popcll(__ballot(kp));               // the whole wave votes, outside the lane-0 store
     if (lane == 0) misc[2] = ns;
   }
   __syncthreads();
 
-  // attention over the selected leaves: per-head softmax statistics, then P in place
+  // ---- softmax over the selected leaves' keys, per head
   const int nsel = misc[2];
   const int nkeys = nsel * kLeaf;
-  for (int h = wave; h < G; h += 4) {
+  for (int h = wave; h < G; h += kDecodeWaves) {
     float m = kNegInf;
     for (int e = lane; e < nkeys; e += 64) m = fmaxf(m, zl[(sels[e / kLeaf] * kLeaf + e % kLeaf) * G + h]);
     for (int o = 1; o < 64; o <<= 1) m = wave_max_xor(m, o);
     float s = 0.f;
-    for (int e = lane; e < nkeys; e += 64) s += expf(zl[(sels[e / kLeaf] * kLeaf + e % kLeaf) * G + h] - m);
+    for (int e = lane; e < nkeys; e += 64) s += __builtin_amdgcn_exp2f(zl[(sels[e / kLeaf] * kLeaf + e % kLeaf) * G + h] - m);
     for (int o = 1; o < 64; o <<= 1) s = wave_add_xor(s, o);
     if (lane == 0) { hstat[h] = m; hstat[G + h] = 1.f / s; }
   }
@@ -255,30 +233,37 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(DecodeArgs a) {
   for (int e = tid; e < nkeys * G; e += blockDim.x) {
     const int h = e % G, kk = e / G;
     float* z = &zl[(sels[kk / kLeaf] * kLeaf + kk % kLeaf) * G + h];
-    *z = expf(*z - hstat[h]) * hstat[G + h];
+    *z = __builtin_amdgcn_exp2f(*z - hstat[h]) * hstat[G + h];
   }
   __syncthreads();
 
-  constexpr int kCols = D / 64;        // value columns per lane
+  // ---- P V: one selected block per wave, 16 value rows in flight
+  constexpr int kCols = D / 64;                         // value columns per lane
+  constexpr int kRows = 16;
   float accv[G][kCols];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int c = 0; c < kCols; ++c) accv[h][c] = 0.f;
-  const T* vbase = reinterpret_cast<const T*>(a.v_cache) + b * a.vc_sb + kvh * a.vc_sh;
-  for (int kk = wave; kk < nkeys; kk += 4) {
-    const int slot = sels[kk / kLeaf];
-    const int64_t key = (int64_t)cand[slot] * kLeaf + kk % kLeaf;
-    if (key > t) continue;
-    const T* vrow = vbase + key * a.vc_st + lane * kCols;
-    float vv[kCols];
+  const T* vbase = reinterpret_cast<const T*>(a.v_cache) + b * a.vc_sb + kvh * a.vc_sh + lane * kCols;
+  for (int j = wave; j < nsel; j += kDecodeWaves) {
+    const int slot = sels[j];
+    const int first = selv[j] * kLeaf;
+    for (int r0 = 0; r0 < kLeaf; r0 += kRows) {
+      float vv[kRows][kCols];
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) vv[c] = to_f32(vrow[c]);
-    const float* p = &zl[(slot * kLeaf + kk % kLeaf) * G];
+      for (int i = 0; i < kRows; ++i)                   // keys past t: clamped row, probability 0
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int c = 0; c < kCols; ++c) vv[i][c] = to_f32(vbase[(int64_t)min(first + r0 + i, t) * a.vc_st + c]);
 #pragma unroll
-      for (int c = 0; c < kCols; ++c) accv[h][c] = fmaf(p[h], vv[c], accv[h][c]);
+      for (int i = 0; i < kRows; ++i) {
+        const float* p = &zl[(slot * kLeaf + r0 + i) * G];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) accv[h][c] = fmaf(p[h], vv[i][c], accv[h][c]);
+      }
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -288,8 +273,9 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(DecodeArgs a) {
   TO* obase = reinterpret_cast<TO*>(a.o) + b * a.o_sb + (int64_t)kvh * G * a.o_sh;
   for (int e = tid; e < G * D; e += blockDim.x) {
     const int h = e / D, c = e % D;
-    const float v = ((part[(0 * G + h) * D + c] + part[(1 * G + h) * D + c]) + part[(2 * G + h) * D + c]) +
-                    part[(3 * G + h) * D + c];
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) v += part[(w * G + h) * D + c];
     obase[h * a.o_sh + c] = from_f32<TO>(v);
   }
   if (a.sel_out && tid < K) a.sel_out[(int64_t)bh * K + tid] = tid < nsel ? selv[tid] : -1;
@@ -307,7 +293,7 @@ hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(a.batch * a.n_kv_heads), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.batch * a.n_kv_heads), dim3(kDecodeWaves * 64), lds, s, a);
   return hipGetLastError();
 }
 
