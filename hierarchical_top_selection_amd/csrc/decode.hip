@@ -31,17 +31,30 @@ __global__ __launch_bounds__(128) void decode_update_kernel(DecodeArgs a) {
   const int64_t first = (int64_t)leaf * kLeaf;
   float val = leaf_mean_column(kc, a.kc_st, first, (int)(pos - first + 1), c);  // reads this thread's own write
   pyr[(a.lv.offset[0] + leaf) * D + c] = val;
+  // The siblings along the path do not change: load them for every level first, then
+  // recompute the path bottom-up (level l's node is the parent of the level l - 1 path node).
+  float sib[kMaxLevels];
   int idx = leaf;
-  for (int level = 2; level <= a.lv.count; ++level) {
-    const int p = idx >> 1;
-    const int child_size = a.lv.size[level - 2];
-    const float* ch = pyr + a.lv.offset[level - 2] * D;
-    const bool has2 = 2 * p + 1 < child_size;
-    const float c0 = (2 * p == idx) ? val : ch[(int64_t)(2 * p) * D + c];
-    const float c1 = has2 ? ((2 * p + 1 == idx) ? val : ch[(int64_t)(2 * p + 1) * D + c]) : 0.f;
-    val = node_mean(c0, c1, has2);
-    pyr[(a.lv.offset[level - 1] + p) * D + c] = val;
-    idx = p;
+#pragma unroll
+  for (int l = 2; l <= kMaxLevels; ++l) {
+    if (l <= a.lv.count) {
+      const int s = idx ^ 1;
+      sib[l - 2] = s < a.lv.size[l - 2] ? pyr[(a.lv.offset[l - 2] + s) * D + c] : 0.f;
+      idx >>= 1;
+    }
+  }
+  idx = leaf;
+#pragma unroll
+  for (int l = 2; l <= kMaxLevels; ++l) {
+    if (l <= a.lv.count) {
+      const int p = idx >> 1;
+      const bool has2 = 2 * p + 1 < a.lv.size[l - 2];
+      const float c0 = (idx & 1) ? sib[l - 2] : val;
+      const float c1 = (idx & 1) ? val : sib[l - 2];
+      val = node_mean(c0, c1, has2);
+      pyr[(a.lv.offset[l - 1] + p) * D + c] = val;
+      idx = p;
+    }
   }
 }
 
@@ -89,7 +102,8 @@ __device__ inline bool decode_keep(const int* cand, const float* us, int nslots,
 }
 
 template <typename T, typename TO, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
+    DecodeArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
   extern __shared__ __align__(16) float smem[];
   const int width = 2 * a.top_k, K = a.top_k;
@@ -237,7 +251,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(DecodeA
   }
   __syncthreads();
 
-  // ---- P V: one selected block per wave, 16 value rows in flight
+  // ---- P V: one selected block per wave, 16 of its value rows in flight at a time (more rows, or
+  // a register cap for more waves per SIMD, measured slower)
   constexpr int kCols = D / 64;                         // value columns per lane
   constexpr int kRows = 16;
   float accv[G][kCols];

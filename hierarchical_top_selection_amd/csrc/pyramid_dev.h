@@ -12,11 +12,20 @@
 namespace pisa {
 
 // Mean of column c over keys [first, first + cnt): float32 sum in key order, then / cnt.
+// Keys are loaded eight at a time (independent loads in flight); the additions keep key order.
 template <typename T>
 __device__ inline float leaf_mean_column(const T* base, int64_t stride_t, int64_t first, int cnt,
                                          int c) {
   float s = 0.f;
-  for (int r = 0; r < cnt; ++r) s += to_f32(base[(first + r) * stride_t + c]);
+  int r = 0;
+  for (; r + 8 <= cnt; r += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = to_f32(base[(first + r + i) * stride_t + c]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += x[i];
+  }
+  for (; r < cnt; ++r) s += to_f32(base[(first + r) * stride_t + c]);
   return s / (float)cnt;
 }
 
