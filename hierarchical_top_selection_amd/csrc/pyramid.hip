@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void pyramid_leaves_kernel(PyramidArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void pyramid_top_kernel(PyramidArgs a) {
+__global__ __launch_bounds__(1024) void pyramid_top_kernel(PyramidArgs a) {
   const int bh = blockIdx.x;
   float* pyr = a.pyr + (int64_t)bh * a.lv.nodes * D;
   for (int level = kInBlockLevels + 1; level <= a.lv.count; ++level) {
@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void pyramid_top_kernel(PyramidArgs a) {
     const int child_size = a.lv.size[level - 2];
     const float* child = pyr + a.lv.offset[level - 2] * D;
     float* dst = pyr + a.lv.offset[level - 1] * D;
+#pragma unroll 4
     for (int item = threadIdx.x; item < nodes * D; item += blockDim.x) {
       const int p = item / D, c = item % D;
       const bool has2 = 2 * p + 1 < child_size;
@@ -94,7 +95,7 @@ hipError_t launch_pyramid_t(const PyramidArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.lv.count > kInBlockLevels) {
-    hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(a.batch * a.n_kv_heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(a.batch * a.n_kv_heads), dim3(1024), 0, s, a);
     e = hipGetLastError();
   }
   return e;
