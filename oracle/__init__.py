@@ -15,7 +15,13 @@ Modules
                    LSE, top-K, attention, decode).
 ``per_query``      an independently written per-query routine (pure-Python
                    loops, its own pyramid, its own LSE) used to pin ``pisa``
-                   on tiny inputs; also a brute-force flat top-K.
+                   on tiny inputs; also a brute-force flat top-K over exact
+                   leaf LSE.
+
+``pisa.flat_mean_select`` is the single-level baseline of the block-sparse
+framework (every valid leaf scored by its mean-key dot product, head sum,
+top K); it is pinned to the exact-LSE brute force through the closed forms
+of constant-key blocks and of the small-logit limit.
 
 Parity status
 -------------

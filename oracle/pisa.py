@@ -31,6 +31,12 @@ Readings where the pages are silent (each listed in the design notes):
       positions <= t, with the same 1/sqrt(d) scale as the scores.
   R6  Decode appends the new key/value at position n, updates the leaf of n
       and its ancestor path, then routes the new query with every key valid.
+  R7  The flat (single-level) baseline of the block-sparse framework scores
+      every causally valid leaf j by its summary dot product q . k_bar_j *
+      scale [Prereq/BSA, top-K block selection], with k_bar_j the leaf mean
+      of the pyramid (built over the whole block, like every summary), sums
+      the scores over the group's heads [Prereq/GQA] and keeps K by
+      (score desc, index asc).
 """
 from __future__ import annotations
 
@@ -133,7 +139,8 @@ def _select_k(u: np.ndarray, ids: np.ndarray, K: int):
     order = np.lexsort((key_ids, -u), axis=-1)
     su = np.take_along_axis(u, order, axis=-1)
     if u.shape[1] > K:
-        gap = su[:, K - 1] - su[:, K]
+        with np.errstate(invalid="ignore"):           # -inf - -inf on rows with <= K valid entries
+            gap = su[:, K - 1] - su[:, K]
         gap = np.where(np.isfinite(su[:, K]), gap, np.inf)
     else:
         gap = np.full(u.shape[0], np.inf)
@@ -234,6 +241,46 @@ def route(q: np.ndarray, k: np.ndarray, pyr: list[np.ndarray], ts: np.ndarray, K
     if record:
         return sel, gap, {"leaf_cand": leaf_cand, "leaf_u": leaf_u, "counts": counts[::-1]}
     return sel, gap
+
+
+def flat_mean_select(q: np.ndarray, leaves: np.ndarray, ts: np.ndarray, K: int, C: int = 64,
+                     scale: float | None = None, return_scores: bool = False):
+    """Single-level block selection of the block-sparse framework [Prereq/BSA; R7].
+
+    q       [T, G, d]  the group's query heads at each token (float64)
+    leaves  [M_1, d]   leaf means (level 1 of ``build_pyramid``)
+    ts      [T]        query positions
+
+    Every leaf j with j * C <= t is scored by u_j = sum over heads of
+    q_h . k_bar_j * scale; K are kept by (u desc, j asc) [R3].  Returns ``sel``
+    [T, K] (ascending, -1 padded) and ``gap`` [T] (K-th minus (K+1)-th score, inf
+    when at most K leaves are valid); with ``return_scores`` also the scores of
+    the selected leaves in ``sel`` order (-inf on padding).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    leaves = np.asarray(leaves, dtype=np.float64)
+    ts = np.asarray(ts, dtype=np.int64)
+    T, G, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    M = leaves.shape[0]
+    z = np.einsum("tgd,md->tgm", q, leaves) * scale                   # [T, G, M]
+    u = z.sum(axis=1)                                                   # [T, M]
+    ids = np.broadcast_to(np.arange(M), (T, M))
+    valid = ids * C <= ts[:, None]
+    u = np.where(valid, u, NEG_INF)
+    ids = np.where(valid, ids, -1)
+    order, gap = _select_k(u, ids, K)
+    top_ids = np.take_along_axis(ids, order[:, :K], axis=-1)
+    top_u = np.take_along_axis(u, order[:, :K], axis=-1)
+    sel = np.full((T, K), -1, dtype=np.int64)
+    sel_u = np.full((T, K), NEG_INF)
+    for r in range(T):
+        keep = top_ids[r] >= 0
+        pairs = sorted(zip(top_ids[r][keep].tolist(), top_u[r][keep].tolist()))
+        sel[r, :len(pairs)] = [j for j, _ in pairs]
+        sel_u[r, :len(pairs)] = [v for _, v in pairs]
+    return (sel, gap, sel_u) if return_scores else (sel, gap)
 
 
 def leaf_lse(q: np.ndarray, k: np.ndarray, j: int, t: int, C: int = 64,

@@ -274,3 +274,75 @@ def test_decode_step_equals_prefill_of_last_token():
         np.testing.assert_array_equal(sel, want_sel[0])
         want_o, _, _ = pisa.attention(q[n:n + 1], k[:n + 1], v[:n + 1], want_sel, np.array([n]), C)
         np.testing.assert_allclose(o, want_o[0], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- flat (single-level) baseline
+@pytest.mark.parametrize("C,G,m1", [(4, 1, 12), (4, 3, 16), (8, 2, 9)])
+def test_flat_mean_equals_exact_lse_on_constant_key_blocks(C, G, m1):
+    """Prerequisites (LSE paragraph): the LSE of m equal logits z is z + log m.  When every key of a
+    block is the same vector, each full block's exact LSE is its mean score plus the same G log C,
+    so the single-level mean selection must equal the independent brute-force exact-LSE flat top-K
+    at every token that ends a block (all valid blocks full)."""
+    rng = np.random.default_rng(300 + C + G + m1)
+    d = 6
+    block_keys = rng.standard_normal((m1, d))
+    k = np.repeat(block_keys, C, axis=0)
+    n = m1 * C
+    q = rng.standard_normal((n, G, d)) + 0.4
+    ts = np.arange(C - 1, n, C)
+    leaves = pisa.build_pyramid(k, C, 2)[0]
+    for K in (1, 3, m1):
+        sel, gap = pisa.flat_mean_select(q[ts], leaves, ts, K, C)
+        for r, t in enumerate(ts):
+            want = per_query.flat_select(k.tolist(), q[t].tolist(), int(t), K, C)
+            assert [int(x) for x in sel[r] if x >= 0] == want, (K, t, gap[r])
+
+
+def test_flat_mean_is_the_small_logit_limit_of_exact_lse():
+    """Prerequisites (LSE paragraph): log sum exp z = log m + mean(z) + Var(z)/2 + ..., so for tiny
+    logits the exact-LSE ranking of full blocks follows the mean score (first-order term).  Checked
+    against the independent brute force wherever the mean ranking's K-th gap dwarfs the variance term."""
+    rng = np.random.default_rng(301)
+    C, G, d, m1, K = 4, 2, 5, 20, 4
+    k = rng.standard_normal((m1 * C, d))
+    q = rng.standard_normal((m1 * C, G, d))
+    scale = 1e-4
+    ts = np.arange(C - 1, m1 * C, C)
+    leaves = pisa.build_pyramid(k, C, 2)[0]
+    sel, gap = pisa.flat_mean_select(q[ts], leaves, ts, K, C, scale)
+    checked = 0
+    for r, t in enumerate(ts):
+        if gap[r] < 1e-6:                       # variance term is O(scale^2 |q|^2 |k|^2) ~ 1e-7
+            continue
+        want = per_query.flat_select(k.tolist(), q[t].tolist(), int(t), K, C, scale)
+        assert [int(x) for x in sel[r] if x >= 0] == want, t
+        checked += 1
+    assert checked >= len(ts) // 2
+
+
+def test_flat_mean_size_validity_planted_block_and_ties():
+    """Selection-set invariants of the flat baseline: min(K, floor(t/C)+1) distinct ascending valid
+    leaves; a strongly planted block is always kept once valid; duplicated blocks tie to the lower
+    index (tie rule reading)."""
+    rng = np.random.default_rng(302)
+    C, G, d, n, K = 4, 2, 8, 120, 3
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    k = rng.standard_normal((n, d))
+    k[5 * C:6 * C] += 6.0 * u                   # block 5
+    q = rng.standard_normal((n, G, d)) + 4.0 * u
+    ts = np.arange(n)
+    leaves = pisa.build_pyramid(k, C, 2)[0]
+    sel, gap = pisa.flat_mean_select(q, leaves, ts, K, C)
+    for t in ts:
+        s = [int(x) for x in sel[t] if x >= 0]
+        assert len(s) == min(K, t // C + 1)
+        assert s == sorted(set(s)) and all(j * C <= t for j in s)
+        if t >= 5 * C:
+            assert 5 in s
+    k2 = rng.standard_normal((8 * C, d))
+    k2[6 * C:7 * C] = k2[2 * C:3 * C]           # block 6 duplicates block 2
+    leaves2 = pisa.build_pyramid(k2, C, 2)[0]
+    qq = np.tile(leaves2[2], (1, 1, 1))         # the query points at block 2's mean: it ranks first
+    sel2, gap2 = pisa.flat_mean_select(qq, leaves2, np.array([8 * C - 1]), 1, C)
+    assert list(sel2[0]) == [2] and gap2[0] == 0.0
