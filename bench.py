@@ -101,6 +101,9 @@ def _device_inputs(w: W.Workload):
     return dev(q), dev(k), dev(v)
 
 
+_INPUTS = {}   # device Q and K of each workload run, reused by the selection sweep
+
+
 def attention_flops(sel, n: int, group: int, d: int) -> float:
     """4 d flops per (query head, valid key): keys of the selected blocks at positions <= t."""
     import torch
@@ -119,6 +122,7 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     from hierarchical_top_selection_amd import binding
 
     q, k, v = _device_inputs(w)
+    _INPUTS[w.name] = (q, k)
     B, N, Hq, d = q.shape
     K = w.top_k
     pyr = torch.empty((B, w.n_kv_heads, binding.pyramid_nodes(N), d), dtype=torch.float32, device=q.device)
@@ -156,6 +160,50 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     flops = attention_flops(sel, N, w.group, d)
     return {"workload": w, "ms_per_step": wall_ms, "pyramid_ms": pyr_ms, "select_ms": sel_ms,
             "attn_ms": attn_ms, "tokens_per_s": B * N / (wall_ms / 1e3), "attn_flops": flops}
+
+
+def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
+    """Selection latency, hierarchical vs single-level, on prefixes N = 4K .. full of one input.
+
+    Both sides build the key pyramid (the flat scan reads its leaf means) and then
+    select K leaves per token: `select_blocks` (routing + exact leaf LSE + top-K)
+    against `select_flat` (every valid leaf scored by its mean key).  Median of `reps`
+    timed runs after one warm-up, HIP events on the current stream.
+    """
+    import torch
+
+    from hierarchical_top_selection_amd import binding
+
+    B, N, Hq, d = q.shape
+    ns = [n for n in (4096, 8192, 16384, 32768, 65536, 131072, 262144) if n <= N]
+    out = {"K": K, "n": ns, "pisa_select_ms": [], "flat_select_ms": [], "flat_over_pisa": []}
+    for n in ns:
+        qn, kn = q[:, :n], k[:, :n]
+        cfg = binding.make_cfg(B, n, Hq, n_kv_heads, d, K, q.dtype)
+        ws_h = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+        ws_f = torch.empty(binding.flat_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+        pyr = torch.empty((B, n_kv_heads, binding.pyramid_nodes(n), d), dtype=torch.float32, device=q.device)
+        sel = torch.empty((B, n_kv_heads, n, K), dtype=torch.int32, device=q.device)
+        runs = {
+            "pisa_select_ms": lambda: (binding.build_pyramid(kn, out=pyr),
+                                       binding.select_blocks(qn, kn, pyr, K, workspace=ws_h, out=sel)),
+            "flat_select_ms": lambda: (binding.build_pyramid(kn, out=pyr),
+                                       binding.select_flat(qn, pyr, n_kv_heads, K, workspace=ws_f, out=sel)),
+        }
+        for key, fn in runs.items():
+            fn()
+            times = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            out[key].append(sorted(times)[len(times) // 2])
+        out["flat_over_pisa"].append(out["flat_select_ms"][-1] / out["pisa_select_ms"][-1])
+        del ws_h, ws_f, pyr, sel
+    return out
 
 
 def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
@@ -236,6 +284,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing record")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the hierarchical vs single-level selection sweep (K = 8, N = 4K .. the workload's N)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times), for scaling HBM byte counters")
     args = ap.parse_args()
@@ -266,6 +316,10 @@ def main() -> int:
         r = run_workload(W.WORKLOADS[name], args.steps, args.warmup)
         extra[name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                        "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"]}
+    if not args.no_sweep:
+        q_main, k_main = _INPUTS[w.name]
+        extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
+    _INPUTS.clear()
     if not args.no_decode:
         extra["decode_b64_ctx131072"] = run_decode(W.WORKLOADS["decode_b64_ctx131072"])
     attn_tflops = main_run["attn_flops"] / (main_run["attn_ms"] * 1e-3) / 1e12

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "pisa_select_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
     "pisa_select_blocks": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pisa_flat_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
+    "pisa_select_flat": (ctypes.c_int, [_P(PisaCfg), PisaTensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pisa_attn_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
     "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
                                             PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -168,6 +171,29 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: in
     _check("pisa_select_blocks", lib().pisa_select_blocks(
         ctypes.byref(cfg), _tensor(q), _tensor(k), ctypes.c_void_p(pyr.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(scores.data_ptr() if scores is not None else 0),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return (out, scores) if return_scores else out
+
+
+def flat_workspace_bytes(cfg: PisaCfg) -> int:
+    return int(lib().pisa_flat_workspace_bytes(ctypes.byref(cfg)))
+
+
+def select_flat(q: torch.Tensor, pyr: torch.Tensor, n_kv_heads: int, top_k: int, scale: float = 0.0,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                return_scores: bool = False):
+    """Single-level (flat) top-K leaf selection by mean-key scores: int32 [B, Hkv, N, K] (and scores)."""
+    B, N, Hq, d = q.shape
+    cfg = make_cfg(B, N, Hq, n_kv_heads, d, top_k, q.dtype, scale)
+    need = flat_workspace_bytes(cfg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, n_kv_heads, N, top_k), dtype=torch.int32, device=q.device)
+    scores = torch.empty((B, n_kv_heads, N, top_k), dtype=torch.float32, device=q.device) if return_scores else None
+    _check("pisa_select_flat", lib().pisa_select_flat(
+        ctypes.byref(cfg), _tensor(q), ctypes.c_void_p(pyr.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(scores.data_ptr() if scores is not None else 0),
         ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
     return (out, scores) if return_scores else out
 

@@ -246,6 +246,37 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   return hip_status(pisa::launch_topk(t, s));
 }
 
+size_t pisa_flat_workspace_bytes(const pisa_cfg* cfg) {
+  if (check_cfg(cfg) != PISA_OK) return 0;
+  const size_t bh = (size_t)cfg->batch * cfg->n_kv_heads;
+  const size_t groups = (cfg->seq_len + 15) / 16;
+  const size_t tiles = ((cfg->seq_len + pisa::kLeaf - 1) / pisa::kLeaf + 15) / 16;
+  return align256(bh * groups * 16 * cfg->head_dim * 4) + align256(bh * tiles * 16 * cfg->head_dim * 4);
+}
+
+pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* pyr, int32_t* sel, float* sel_u,
+                             void* ws, size_t ws_bytes, void* stream) {
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  if (cfg->top_k > 16) return PISA_ERR_UNSUPPORTED;
+  if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
+  if (!aligned16(pyr) || !sel) return PISA_ERR_INVALID_ARG;
+  const size_t need = pisa_flat_workspace_bytes(cfg);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return PISA_ERR_WORKSPACE;
+  const size_t bh = (size_t)cfg->batch * cfg->n_kv_heads;
+  const size_t groups = (cfg->seq_len + 15) / 16;
+  pisa::FlatArgs a;
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_st = q.stride_t; a.q_sh = q.stride_h;
+  a.pyr = pyr; a.nodes = make_levels(cfg->seq_len, cfg->seq_len).nodes;
+  a.qsum = static_cast<float4*>(ws);
+  a.kpack = reinterpret_cast<float4*>(static_cast<char*>(ws) + align256(bh * groups * 16 * cfg->head_dim * 4));
+  a.sel = sel; a.sel_u = sel_u;
+  a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
+  a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  return hip_status(pisa::launch_flat(a, (hipStream_t)stream));
+}
+
 size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg) {
   if (check_cfg(cfg) != PISA_OK) return 0;
   if (cfg->dtype != PISA_BF16) return 0;

@@ -130,6 +130,21 @@ struct QPackArgs {
 // P V product of key half kb.
 __host__ __device__ inline int perm_key(int mt, int m) { return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3); }
 
+// Single-level (flat) selection: summed query groups and leaf means in MFMA fragment order.
+struct FlatArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  const float* pyr;         // pyramid built with capacity n (leaf level first)
+  int64_t nodes;            // pyramid nodes per (b, kvh)
+  float4* qsum;             // workspace: [B*Hkv][ceil(n/16)][d/16][64] summed heads, fp32
+  float4* kpack;            // workspace: [B*Hkv][ceil(M1/16)][d/16][64] leaf means, fp32
+  int32_t* sel;             // [B*Hkv][n][K] ascending, -1 padded
+  float* sel_u;             // optional scores
+  int batch, n_kv_heads, group, head_dim, n, top_k;
+  float scale;
+  bool bf16;
+};
+
 struct DecodeArgs {
   const void* q;            // [B][Hq][d]
   int64_t q_sb, q_sh;
@@ -163,6 +178,7 @@ hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_flat(const FlatArgs& a, hipStream_t s);
 
 // LDS bytes of the fused decode kernel for (group, 2K, d).
 size_t decode_lds_bytes(int group, int width, int head_dim);

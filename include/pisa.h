@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 1
+#define PISA_ABI_VERSION 2
 
 typedef enum {
   PISA_OK = 0,
@@ -142,6 +142,28 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  */
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
                                int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by pisa_select_flat for cfg (summed query groups and leaf
+ * means, both float32 in MFMA fragment order). */
+size_t pisa_flat_workspace_bytes(const pisa_cfg* cfg);
+
+/*
+ * select_flat - the single-level block selection of the block-sparse framework
+ * (Prerequisites: block sparse attention / top-K block selection and
+ * grouped-query attention), the O(N^2 / C) scan that hierarchical routing
+ * replaces; provided as the baseline to measure routing against.  Every leaf j
+ * with 64 j <= t is scored by u = sum over the group's query heads of
+ * q_h . k_bar_j * scale, k_bar_j the leaf mean of the pyramid (built over the
+ * whole block), and K leaves are kept by (u descending, index ascending).
+ *   q       : [B][N][H_q][d], cfg->dtype
+ *   pyr     : pyramid of k built with n = N (capacity N); only the leaves are read
+ *   sel     : int32 [B][H_kv][N][K] output, ascending, -1 padded
+ *   sel_u   : optional float32 [B][H_kv][N][K] output (NULL to skip), -inf on padding
+ *   ws      : workspace of >= pisa_flat_workspace_bytes(cfg) bytes
+ * Returns PISA_ERR_UNSUPPORTED for K > 16.
+ */
+pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* pyr, int32_t* sel, float* sel_u,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by pisa_sparse_attn_fwd for cfg: bf16 inputs stage K and
  * V as packed 64-key blocks, each fragment of the attention products one

@@ -16,10 +16,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_symbols()
-    assert len(declared) == 11
+    assert len(declared) == 13
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 1
+    assert lib.pisa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -92,3 +92,19 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
     assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == 2 * 4096 * 128 * 2
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
                                     None, None, 0, None) == 3
+
+
+def test_flat_selection_validation_and_workspace(lib):
+    """The flat baseline keeps at most 16 leaves and needs its two packed buffers."""
+    cfg = _cfg()
+    good = binding.PisaTensor(4096, 0, 128, 128)
+    groups, tiles = -(-cfg.seq_len // 16), -(-(-(-cfg.seq_len // 64)) // 16)
+    want = (-(-groups * 16 * cfg.head_dim * 4 // 256) + -(-tiles * 16 * cfg.head_dim * 4 // 256)) * 256
+    assert lib.pisa_flat_workspace_bytes(ctypes.byref(cfg)) == want
+    assert lib.pisa_select_flat(ctypes.byref(cfg), good, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                                ctypes.c_void_p(4096), 16, None) == 3                      # workspace too small
+    assert lib.pisa_select_flat(ctypes.byref(cfg), good, ctypes.c_void_p(4096), None, None,
+                                ctypes.c_void_p(4096), 1 << 30, None) == 1                 # no output
+    wide = _cfg(top_k=17)
+    assert lib.pisa_select_flat(ctypes.byref(wide), good, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                                ctypes.c_void_p(4096), 1 << 30, None) == 2                 # K > 16

@@ -1,0 +1,77 @@
+"""GPU parity of the single-level (flat) block selection baseline against the oracle.
+
+Every case draws seeded inputs (hierarchical_top_selection_amd.workloads), runs the
+pyramid and pisa_select_flat through the C ABI, and compares with
+oracle.pisa.flat_mean_select on the same values: selections bit-exact except where the
+oracle's K-th vs (K+1)-th score gap is below 1e-3 (at most 0.1% of the queries), and
+the scores of the selected leaves within 1e-4 + 1e-5 |u|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_top_selection_amd import binding
+from hierarchical_top_selection_amd import workloads as W
+from oracle import pisa as oracle
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def check_flat(w: W.Workload, K: int, label: str, sample: int | None = None):
+    H.log(f"[{label}] inputs B={w.batch} N={w.seq_len} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} K={K}")
+    q, k, _ = W.prefill_inputs(w, bits=True)
+    qd, kd = H.to_device(q, w), H.to_device(k, w)
+    pyr = binding.build_pyramid(kd)
+    sel, sel_u = binding.select_flat(qd, pyr, w.n_kv_heads, K, return_scores=True)
+    torch.cuda.synchronize()
+    sel, sel_u = sel.cpu().numpy(), sel_u.cpu().numpy()
+    G = w.group
+    n_bad = n_total = 0
+    for b in range(w.batch):
+        for kvh in range(w.n_kv_heads):
+            ts = np.arange(w.seq_len) if sample is None else H.sample_tokens(w.seq_len, sample, 7 + b + kvh)
+            qg = H.host_values(q[b, :, kvh * G:(kvh + 1) * G, :]).astype(np.float64)[ts]
+            kk = H.host_values(k[b, :, kvh]).astype(np.float64)
+            leaves = oracle.build_pyramid(kk)[0]
+            osel, gap, ou = oracle.flat_mean_select(qg, leaves, ts, K, return_scores=True)
+            gsel, gu = sel[b, kvh][ts], sel_u[b, kvh][ts]
+            bad, agree = H.compare_selection(gsel, osel, gap, f"{label} b={b} kvh={kvh}")
+            n_bad += bad
+            n_total += len(ts)
+            fin = np.isfinite(ou[agree])
+            assert np.array_equal(fin, np.isfinite(gu[agree])), label
+            du = np.abs(gu[agree][fin] - ou[agree][fin])
+            assert du.size == 0 or np.all(du <= 1e-4 + 1e-5 * np.abs(ou[agree][fin])), (label, float(du.max()))
+            counts = (gsel >= 0).sum(axis=1)
+            assert np.array_equal(counts, np.minimum(K, ts // 64 + 1)), label
+    H.assert_mismatch_budget(n_bad, n_total, label)
+
+
+def test_flat_tiny_f32():
+    check_flat(W.WORKLOADS["tiny_f32_n1024"], 4, "flat_tiny_f32")
+
+
+@pytest.mark.parametrize("K", [8, 16])
+def test_flat_prefill_n4096(K):
+    check_flat(W.WORKLOADS["prefill_n4096"], K, f"flat_n4096_k{K}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=2, seq_len=4133, n_q_heads=8, n_kv_heads=2, head_dim=128, top_k=5),
+    dict(batch=1, seq_len=3000, n_q_heads=8, n_kv_heads=8, head_dim=64, top_k=1),
+    dict(batch=1, seq_len=2600, n_q_heads=16, n_kv_heads=1, head_dim=64, top_k=16),
+    dict(batch=1, seq_len=700, n_q_heads=4, n_kv_heads=1, head_dim=128, top_k=16),
+])
+def test_flat_shapes(shape):
+    K = shape.pop("top_k")
+    w = W.WORKLOADS["prefill_n4096"].with_(name="flat_shape", seed=61, **shape)
+    check_flat(w, K, f"flat_b{w.batch}_n{w.seq_len}_g{w.group}_d{w.head_dim}_k{K}")
+
+
+@pytest.mark.parametrize("name,K", [("prefill_n32768", 16), ("prefill_n262144", 8)])
+def test_flat_full_size_sampled(name, K):
+    check_flat(W.WORKLOADS[name], K, f"flat_{name}_k{K}", sample=600)
