@@ -18,6 +18,12 @@ Modules
                    on tiny inputs; also a brute-force flat top-K over exact
                    leaf LSE.
 
+``score="mean"`` / ``"mean_var"`` (both routines) are the PISA-1 / PISA-2
+score variants (mean, and mean + half the population variance, of the
+children's logits), pinned by the second-order Taylor expansion of the LSE,
+by agreement of the two routines, and by equality of PISA-1 without cuts
+with the flat mean-key selection.
+
 ``pisa.flat_mean_select`` is the single-level baseline of the block-sparse
 framework (every valid leaf scored by its mean-key dot product, head sum,
 top K); it is pinned to the exact-LSE brute force through the closed forms

@@ -76,17 +76,27 @@ def lse_exact(values, digits: int = 50):
         return float(total.ln())
 
 
-def score(pyr: Pyramid, heads, level, i, t, scale):
-    """u = sum over heads of LSE over the valid children of node (level, i)."""
+def _reduce(values, mode):
+    """LSE, or the mean / mean + half population variance of the score variants."""
+    if mode == "lse":
+        return lse(values)
+    mean = math.fsum(values) / len(values)
+    if mode == "mean":
+        return mean
+    return mean + 0.5 * math.fsum((v - mean) ** 2 for v in values) / len(values)
+
+
+def score(pyr: Pyramid, heads, level, i, t, scale, mode="lse"):
+    """u = sum over heads of the score (LSE, or a variant) over the valid children of node (level, i)."""
     kids = pyr.children(level, i)
     if level == 1:
         kids = [r for r in kids if r <= t]
     else:
         kids = [c for c in kids if pyr.first(level - 1, c) <= t]
-    return math.fsum(lse([dot(q, pyr.vector(level - 1, c)) * scale for c in kids]) for q in heads)
+    return math.fsum(_reduce([dot(q, pyr.vector(level - 1, c)) * scale for c in kids], mode) for q in heads)
 
 
-def select(keys, heads, t, K, C=64, g=2, scale=None, pyr=None):
+def select(keys, heads, t, K, C=64, g=2, scale=None, pyr=None, mode="lse"):
     """Leaf block ids chosen for query position t (sorted ascending)."""
     pyr = pyr or Pyramid(keys, C, g)
     scale = 1.0 / math.sqrt(len(heads[0])) if scale is None else scale
@@ -94,7 +104,7 @@ def select(keys, heads, t, K, C=64, g=2, scale=None, pyr=None):
     cand = [0]
     while True:
         if len(cand) > K:
-            ranked = sorted(cand, key=lambda i: (-score(pyr, heads, level, i, t, scale), i))
+            ranked = sorted(cand, key=lambda i: (-score(pyr, heads, level, i, t, scale, mode), i))
             cand = ranked[:K]
         if level == 1:
             return sorted(cand)

@@ -31,6 +31,12 @@ Readings where the pages are silent (each listed in the design notes):
       positions <= t, with the same 1/sqrt(d) scale as the scores.
   R6  Decode appends the new key/value at position n, updates the leaf of n
       and its ancestor path, then routes the new query with every key valid.
+  R8  Score variants [Core: Taylor expansion of the LSE score into a mean and a
+      variance correction; the PISA-1 / PISA-2 ablations]: "mean" (PISA-1)
+      scores a candidate by the mean of its valid children's logits and
+      "mean_var" (PISA-2) by that mean plus half their population variance;
+      neither carries the log m term.  Both apply at every scored level,
+      the leaf level included (raw keys <= t), with the same head sum.
   R7  The flat (single-level) baseline of the block-sparse framework scores
       every causally valid leaf j by its summary dot product q . k_bar_j *
       scale [Prereq/BSA, top-K block selection], with k_bar_j the leaf mean
@@ -129,6 +135,31 @@ def logsumexp(z: np.ndarray, axis: int = -1) -> np.ndarray:
     return np.squeeze(out, axis=axis)
 
 
+SCORES = ("lse", "mean", "mean_var")
+
+
+def child_score(z: np.ndarray, ok: np.ndarray, score: str = "lse") -> np.ndarray:
+    """Score of a candidate from its children's logits ``z`` [..., c] (valid where ``ok``).
+
+    "lse": log sum exp over the valid children [Core: eq. 21]; "mean" (PISA-1) and
+    "mean_var" (PISA-2): mean, and mean plus half the population variance, of the
+    valid children's logits [R8].  -inf when no child is valid.
+    """
+    if score == "lse":
+        return logsumexp(np.where(ok, z, NEG_INF), axis=-1)
+    m = ok.sum(axis=-1)
+    zz = np.where(ok, z, 0.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        mean = zz.sum(axis=-1) / m
+        out = mean
+        if score == "mean_var":
+            dev = np.where(ok, z - mean[..., None], 0.0)
+            out = mean + 0.5 * (dev * dev).sum(axis=-1) / m
+        elif score != "mean":
+            raise ValueError(f"unknown score {score!r}")
+    return np.where(m > 0, out, NEG_INF)
+
+
 def _select_k(u: np.ndarray, ids: np.ndarray, K: int):
     """Per row: order candidates by (u desc, id asc) [R3]; returns the order and the K-th gap.
 
@@ -155,7 +186,7 @@ def _pad_rows(rows: list[list[int]], width: int) -> np.ndarray:
 
 
 def route(q: np.ndarray, k: np.ndarray, pyr: list[np.ndarray], ts: np.ndarray, K: int,
-          C: int = 64, g: int = 2, scale: float | None = None, record: bool = False):
+          C: int = 64, g: int = 2, scale: float | None = None, record: bool = False, score: str = "lse"):
     """Top-down hierarchical selection for a batch of query tokens [Core: eq. 16-21; Steps: eq. 22].
 
     q      [T, G, d]  the G query heads of one GQA group at each token (float64)
@@ -168,6 +199,8 @@ def route(q: np.ndarray, k: np.ndarray, pyr: list[np.ndarray], ts: np.ndarray, K
     scale) over its valid children (raw keys at the leaf level), sum s over
     the group's heads (u_i, eq. 22), keep K by (u desc, index asc) and expand
     the survivors to their valid children.  At level 1 the survivors are I_t.
+    ``score`` picks the candidate score: "lse" (the method), "mean" or "mean_var"
+    (the PISA-1 / PISA-2 variants, R8).
 
     Returns ``sel`` [T, K] (ascending, -1 padded) and ``gap`` [T], the
     smallest K-th minus (K+1)-th score difference over the scored levels
@@ -210,8 +243,7 @@ def route(q: np.ndarray, k: np.ndarray, pyr: list[np.ndarray], ts: np.ndarray, K
             R, W, c = ok.shape
             z = np.matmul(vecs.reshape(R, W * c, d), np.transpose(q[rows], (0, 2, 1))) * scale
             z = np.transpose(z.reshape(R, W, c, G), (0, 3, 1, 2))                  # [R, G, W, c]
-            z = np.where(ok[:, None, :, :], z, NEG_INF)
-            s = logsumexp(z, axis=-1)                                              # [R, G, W]
+            s = child_score(z, ok[:, None, :, :], score)                           # [R, G, W]
             ur = s.sum(axis=1)                                                     # [R, W]
             ur = np.where(cr >= 0, ur, NEG_INF)
             order, gr = _select_k(ur, cr, K)
@@ -338,7 +370,7 @@ def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, ts: np.n
 
 # ----------------------------------------------------------------------------- whole prefill / decode
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, K: int, C: int = 64, g: int = 2,
-            ts=None, scale: float | None = None, chunk: int = 32):
+            ts=None, scale: float | None = None, chunk: int = 32, score: str = "lse"):
     """Selection and attention for one (sequence, KV head): q [n, G, d], k/v [n, d].
 
     ``ts`` restricts the queries evaluated (default: all n).  Returns a dict
@@ -350,7 +382,7 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, K: int, C: int = 64, g:
     sels, gaps, outs, lses = [], [], [], []
     for s in range(0, len(ts), chunk):
         tc = ts[s:s + chunk]
-        sel, gap = route(q[tc], k, pyr, tc, K, C, g, scale)
+        sel, gap = route(q[tc], k, pyr, tc, K, C, g, scale, score=score)
         o, lse, _ = attention(q[tc], k, v, sel, tc, C, scale)
         sels.append(sel); gaps.append(gap); outs.append(o); lses.append(lse)
     return {"sel": np.concatenate(sels), "gap": np.concatenate(gaps),
@@ -381,7 +413,7 @@ class DecodeState:
         return self.vbuf[:self.n]
 
     def step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, K: int,
-             scale: float | None = None):
+             scale: float | None = None, score: str = "lse"):
         """Append (k_new, v_new) at position n, update the pyramid, route q at t = n, attend (R6)."""
         self.kbuf[self.n] = k_new
         self.vbuf[self.n] = v_new
@@ -390,6 +422,6 @@ class DecodeState:
         self.pyr = update_pyramid(self.pyr, keys, self.n, self.C, self.g)
         t = np.array([self.n - 1])
         qq = np.asarray(q, dtype=np.float64)[None]
-        sel, gap = route(qq, keys, self.pyr, t, K, self.C, self.g, scale)
+        sel, gap = route(qq, keys, self.pyr, t, K, self.C, self.g, scale, score=score)
         o, lse, _ = attention(qq, keys, self.values(), sel, t, self.C, scale)
         return sel[0], gap[0], o[0], lse[0]

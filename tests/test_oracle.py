@@ -346,3 +346,61 @@ def test_flat_mean_size_validity_planted_block_and_ties():
     qq = np.tile(leaves2[2], (1, 1, 1))         # the query points at block 2's mean: it ranks first
     sel2, gap2 = pisa.flat_mean_select(qq, leaves2, np.array([8 * C - 1]), 1, C)
     assert list(sel2[0]) == [2] and gap2[0] == 0.0
+
+
+# ----------------------------------------------------------------------------- score variants (PISA-1, PISA-2)
+@pytest.mark.parametrize("mode", ["mean", "mean_var"])
+@pytest.mark.parametrize("seed", range(3))
+def test_score_variants_agree_with_independent_per_query_routine(mode, seed):
+    """The mean (PISA-1) and mean + var/2 (PISA-2) scores through the whole hierarchy: the vectorised
+    oracle and the independently written per-query routine agree."""
+    rng = np.random.default_rng(400 + seed)
+    C, G, K, n = [(4, 2, 2, 96), (2, 3, 3, 77), (8, 1, 2, 130)][seed]
+    k = rng.standard_normal((n, 5))
+    k[C * 2:C * 3] += 1.2
+    q = rng.standard_normal((n, G, 5)) + 0.3
+    pyr = pisa.build_pyramid(k, C, 2)
+    sel, gap = pisa.route(q, k, pyr, np.arange(n), K, C, 2, score=mode)
+    ref_pyr = per_query.Pyramid(k.tolist(), C, 2)
+    for t in range(n):
+        want = per_query.select(k.tolist(), q[t].tolist(), t, K, C, 2, pyr=ref_pyr, mode=mode)
+        assert [int(x) for x in sel[t] if x >= 0] == want, (t, gap[t])
+
+
+def test_mean_var_score_is_the_second_order_truncation_of_lse():
+    """Core method (Taylor expansion): LSE(z) = log m + mean + Var/2 + O(z^3).  The PISA-2 score must
+    match LSE - log m with a residual shrinking like the cube of the logit scale, and the PISA-1
+    score must match with a residual shrinking like its square (the variance term)."""
+    rng = np.random.default_rng(401)
+    z0 = rng.standard_normal((50, 7))
+    ok = rng.random((50, 7)) < 0.8
+    ok[:, 0] = True
+    m = ok.sum(axis=1)
+    res2, res1 = [], []
+    for eps in (1e-1, 1e-2):
+        z = eps * z0
+        target = pisa.logsumexp(np.where(ok, z, -np.inf), axis=-1) - np.log(m)
+        res2.append(np.max(np.abs(pisa.child_score(z, ok, "mean_var") - target)))
+        res1.append(np.max(np.abs(pisa.child_score(z, ok, "mean") - target)))
+    assert res2[1] < res2[0] * 2e-3 and res2[1] < 1e-5        # ~eps^3: 1000x smaller for 10x smaller eps
+    assert 5e-3 < res1[1] / res1[0] < 2e-2                   # ~eps^2: 100x smaller
+    assert np.all(pisa.child_score(np.zeros((2, 3)), np.zeros((2, 3), bool), "mean_var") == -np.inf)
+
+
+def test_mean_score_without_cuts_equals_the_flat_mean_selection():
+    """PISA-1 (mean of the logits) at the leaf level is linear in the keys, so when no level above the
+    leaves is cut (K >= ceil(M1/2)) and every valid block is full, the hierarchy returns the flat
+    mean-key selection of the block-sparse framework."""
+    rng = np.random.default_rng(402)
+    C, G, d, m1 = 4, 3, 6, 14
+    n = C * m1
+    k = rng.standard_normal((n, d))
+    q = rng.standard_normal((n, G, d)) + 0.2
+    K = -(-m1 // 2)
+    ts = np.arange(C - 1, n, C)
+    pyr = pisa.build_pyramid(k, C, 2)
+    sel, _ = pisa.route(q[ts], k, pyr, ts, K, C, 2, score="mean")
+    flat, gap = pisa.flat_mean_select(q[ts], pyr[0], ts, K, C)
+    for r in range(len(ts)):
+        if gap[r] > 1e-9:
+            assert list(sel[r]) == list(flat[r]), ts[r]
