@@ -32,7 +32,10 @@ class PisaCfg(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("fanout", ctypes.c_int32), ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("score", ctypes.c_int32)]
+
+
+SCORES = {"lse": 0, "mean": 1, "mean_var": 2}   # PISA, PISA-1, PISA-2 candidate scores
 
 
 class PisaTensor(ctypes.Structure):
@@ -117,9 +120,11 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
 
 
 def make_cfg(batch: int, seq_len: int, n_q_heads: int, n_kv_heads: int, head_dim: int, top_k: int,
-             dtype: torch.dtype, scale: float = 0.0) -> PisaCfg:
+             dtype: torch.dtype, scale: float = 0.0, score: str = "lse") -> PisaCfg:
     code = PISA_BF16 if dtype == torch.bfloat16 else PISA_F32
-    return PisaCfg(batch, seq_len, n_q_heads, n_kv_heads, head_dim, LEAF, FANOUT, top_k, code, scale)
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {sorted(SCORES)}")
+    return PisaCfg(batch, seq_len, n_q_heads, n_kv_heads, head_dim, LEAF, FANOUT, top_k, code, scale, SCORES[score])
 
 
 def pyramid_nodes(capacity: int) -> int:
@@ -157,11 +162,15 @@ def select_workspace_bytes(cfg: PisaCfg) -> int:
 
 def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: int, scale: float = 0.0,
                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                  return_scores: bool = False):
-    """Hierarchical top-K leaf selection: int32 [B, Hkv, N, K] (and float32 scores if asked)."""
+                  return_scores: bool = False, score: str = "lse"):
+    """Hierarchical top-K leaf selection: int32 [B, Hkv, N, K] (and float32 scores if asked).
+
+    ``score``: "lse" (the method), "mean" or "mean_var" (the PISA-1 / PISA-2 variants).
+    """
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     cfg = _cfg_from(q, k, top_k, scale)
+    cfg.score = SCORES[score]
     need = select_workspace_bytes(cfg)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -231,14 +240,14 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
 def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                 v_cache: torch.Tensor, pyr: torch.Tensor, n_ctx: int, top_k: int, scale: float = 0.0,
                 out: torch.Tensor | None = None, sel_out: torch.Tensor | None = None,
-                out_dtype: torch.dtype | None = None):
+                out_dtype: torch.dtype | None = None, score: str = "lse"):
     """One decode step for every sequence: q [B, Hq, d], k_new/v_new [B, Hkv, d], caches [B, cap, Hkv, d].
 
     Appends at position n_ctx, updates the pyramid in place and returns (o [B, Hq, d], sel [B, Hkv, K]).
     """
     B, cap, Hkv, d = k_cache.shape
     Hq = q.shape[1]
-    cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, k_cache.dtype, scale)
+    cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, k_cache.dtype, scale, score)
     _dtype_code(k_cache)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)

@@ -63,6 +63,8 @@ pisa_status check_cfg(const pisa_cfg* c) {
     return PISA_ERR_INVALID_ARG;
   if (c->n_q_heads % c->n_kv_heads != 0) return PISA_ERR_INVALID_ARG;
   if (c->dtype != PISA_F32 && c->dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
+  if (c->score != PISA_SCORE_LSE && c->score != PISA_SCORE_MEAN && c->score != PISA_SCORE_MEAN_VAR)
+    return PISA_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (c->block != pisa::kLeaf || c->fanout != pisa::kFanout) return PISA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PISA_ERR_UNSUPPORTED;
@@ -199,7 +201,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.q = q.ptr; r.q_sb = q.stride_b; r.q_st = q.stride_t; r.q_sh = q.stride_h;
   r.pyr = pyr; r.cand = cand;
   r.batch = cfg->batch; r.n_kv_heads = cfg->n_kv_heads; r.group = G; r.head_dim = cfg->head_dim;
-  r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16;
+  r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16; r.score = cfg->score;
   r.lv = make_levels(N, N);
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
   r.pairs = split_pairs(r.lv, r.pair_off);
@@ -236,7 +238,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   l.batch = cfg->batch; l.n_kv_heads = cfg->n_kv_heads; l.group = G; l.head_dim = cfg->head_dim;
   l.n = N; l.width = width; l.n_leaves = m1; l.window = kWindow; l.n_windows = w.n_windows;
   l.items = items; l.n_items = n_items; l.item_cap = w.item_cap;
-  l.scale = scale; l.bf16 = bf16;
+  l.scale = scale; l.bf16 = bf16; l.score = cfg->score;
   l.kpack = kpack; l.qpack = qpack;
   if ((st = hip_status(pisa::launch_leaf_lse(l, s))) != PISA_OK) return st;
 
@@ -338,6 +340,7 @@ pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, 
   a.o = o.ptr; a.o_sb = o.stride_b; a.o_sh = o.stride_h;
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = G; a.head_dim = cfg->head_dim;
   a.top_k = cfg->top_k; a.n_ctx = n_ctx; a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16;
+  a.score = cfg->score;
   a.out_bf16 = o_dtype == PISA_BF16;
   a.lv = make_levels(n_ctx + 1, cfg->seq_len);
   return hip_status(pisa::launch_decode(a, (hipStream_t)stream));

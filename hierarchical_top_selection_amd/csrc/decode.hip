@@ -66,7 +66,8 @@ __global__ __launch_bounds__(128) void decode_update_kernel(DecodeArgs a) {
 //    head sum a DPP row reduction; wave 0 ranks (score descending, index ascending) and expands;
 //  * leaf scoring: one candidate leaf per wave, S^T over its 64 raw keys on the input type's MFMA;
 //    the logits (base-2 units) are staged in LDS and reused by the attention, so the selected keys
-//    are read from HBM once;
+//    are read from HBM once; every level scores with the configured candidate score (LSE, or the
+//    mean / mean + var/2 variants);
 //  * attention: softmax statistics per head over the selected leaves' staged logits, then P V with
 //    one selected block per wave, 16 value rows in flight at a time, and a fixed-order sum of the
 //    per-wave partial outputs.
@@ -153,10 +154,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {                   // candidate 8 nt + 2 g + h: rows 4 g + 2 h, +1
           const int r0 = 4 * g + 2 * h;
-          const float z0 = ((okmask >> r0) & 1) ? acc[2 * h] * c2 : kNegInf;
-          const float z1 = ((okmask >> (r0 + 1)) & 1) ? acc[2 * h + 1] * c2 : kNegInf;
-          const float m = fmaxf(z0, z1);
-          const float sc = m == kNegInf ? kNegInf : m + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(z0, z1) - m));
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], (okmask >> r0) & 1, (okmask >> (r0 + 1)) & 1,
+                                      a.score, a.scale, c2);
           const float u = row_sum_to_last(head_ok ? sc : 0.f);
           if (col == 15) us[8 * nt + 2 * g + h] = u;
         }
@@ -195,28 +194,61 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
       kf.load(kbase + (int64_t)min(first + 16 * mt + col, t) * a.kc_st, g);
       acc[mt] = mma(kf, qr, floatx4{0.f, 0.f, 0.f, 0.f});
     }
-    // acc[mt][r]: key first + 16 mt + 4 g + r, head col
-    float m = kNegInf;
+    // acc[mt][r]: key first + 16 mt + 4 g + r, head col; the attention reuses the staged logits
+    float head;                                         // this head's leaf score
+    if (a.score == 0) {                                 // LSE, base-2 units
+      float m = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 16 * mt + 4 * g + r;
-        const float z = first + key <= t ? acc[mt][r] * c2 : kNegInf;
-        acc[mt][r] = z;
-        m = fmaxf(m, z);
-        if (head_ok) zl[(slot * kLeaf + key) * G + col] = z;
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * mt + 4 * g + r;
+          const float z = first + key <= t ? acc[mt][r] * c2 : kNegInf;
+          if (head_ok) zl[(slot * kLeaf + key) * G + col] = z;
+          acc[mt][r] = z;
+          m = fmaxf(m, z);
+        }
+      m = wave_max_xor(m, 16);
+      m = wave_max_xor(m, 32);
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(acc[mt][r] - m);   // key t is valid: m finite
+      sum = wave_add_xor(sum, 16);
+      sum = wave_add_xor(sum, 32);
+      head = m + __builtin_amdgcn_logf(sum);
+    } else {                                            // mean, or mean + var / 2, natural units
+      const float cnt = (float)min(kLeaf, t - first + 1);
+      float s1 = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * mt + 4 * g + r;
+          const bool ok = first + key <= t;
+          if (head_ok) zl[(slot * kLeaf + key) * G + col] = ok ? acc[mt][r] * c2 : kNegInf;
+          s1 += ok ? acc[mt][r] : 0.f;
+        }
+      s1 = wave_add_xor(s1, 16);
+      s1 = wave_add_xor(s1, 32);
+      const float mean = s1 / cnt;
+      head = mean * a.scale;
+      if (a.score == 2) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dv = (acc[mt][r] - mean) * a.scale;
+            s2 += first + 16 * mt + 4 * g + r <= t ? dv * dv : 0.f;
+          }
+        s2 = wave_add_xor(s2, 16);
+        s2 = wave_add_xor(s2, 32);
+        head += 0.5f * s2 / cnt;
       }
-    m = wave_max_xor(m, 16);
-    m = wave_max_xor(m, 32);
-    float sum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(acc[mt][r] - m);   // key t is valid: m finite
-    sum = wave_add_xor(sum, 16);
-    sum = wave_add_xor(sum, 32);
-    const float u = row_sum_to_last(head_ok ? m + __builtin_amdgcn_logf(sum) : 0.f);
+    }
+    const float u = row_sum_to_last(head_ok ? head : 0.f);
     if (lane == 15) us[slot] = u;
   }
   __syncthreads();

@@ -32,6 +32,7 @@ struct RouteArgs {
   int64_t pairs;
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
   int batch, n_kv_heads, group, head_dim, n, top_k;
+  int score;          // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
   bool bf16;
   Levels lv;
@@ -63,6 +64,7 @@ struct LeafArgs {
   const bf16x8* kpack;   // bf16 inputs: packed K blocks (PackArgs layout)
   const bf16x8* qpack;   // bf16 inputs: packed query groups (QPackArgs layout)
   int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows, item_cap;
+  int score;             // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
   bool bf16;
 };
@@ -161,6 +163,7 @@ struct DecodeArgs {
   void* o;                  // [B][Hq][d]
   int64_t o_sb, o_sh;
   int batch, n_kv_heads, group, head_dim, top_k, n_ctx;
+  int score;                // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
   bool bf16;                // element type of q, k/v (new and cached)
   bool out_bf16;            // element type of o

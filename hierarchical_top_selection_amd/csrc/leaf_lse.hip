@@ -11,7 +11,8 @@
 // (keys on rows, heads on columns), so a lane owns 16 keys of one head: the
 // per-head max and sum over the 64 keys are in-lane plus two cross-group
 // shuffles, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
-// 16-lane reduction; lane 0 writes the pair's score.  bf16 inputs use
+// 16-lane reduction; one lane writes the pair's score.  The mean and mean + var/2 score
+// variants (PISA-1 / PISA-2) reduce the same logits to their mean and variance instead.  bf16 inputs use
 // v_mfma_f32_16x16x32_bf16 (exact products, fp32 sums); fp32 inputs
 // v_mfma_f32_16x16x4_f32.
 #include "kernels.h"
@@ -35,36 +36,65 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     acc[mt] = mma(kf[mt], qf, acc[mt]);
   }
-  // acc[mt][r]: key start + key_offset(mt, 4 g + r) against head column col (packed bf16
-  // blocks hold keys in perm_key order, fp32 keys are in order).  Keys past min(t, n - 1)
-  // are masked; `last` is n - 1 - start capped at 63.
+  // acc[mt][r]: key start + key_off(mt, r) against head column col (packed bf16 blocks hold
+  // keys in perm_key order, fp32 keys are in order).  Keys past min(t, n - 1) are left out;
+  // `last` is n - 1 - start capped at 63.
+  auto key_off = [&](int mt, int r) {
+    return sizeof(T) == 2 ? 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + r : 16 * mt + 4 * g + r;
+  };
   const int lim = min(t - start, last);
-  if (lim < kLeaf - 1) {
+  float head;                                           // this head's score, natural units
+  if (a.score == 0) {                                   // LSE
+    if (lim < kLeaf - 1) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key_off(mt, r) > lim) acc[mt][r] = kNegInf;
+    }
+    float m = kNegInf;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int off = sizeof(T) == 2 ? 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + r : 16 * mt + 4 * g + r;
-        if (off > lim) acc[mt][r] = kNegInf;
-      }
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][r]);
+    m = wave_max_xor(m, 16);
+    m = wave_max_xor(m, 32);
+    const float mc = m * c2;
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
+    s = wave_add_xor(s, 16);
+    s = wave_add_xor(s, 32);
+    // natural-log LSE: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
+    head = (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f;
+  } else {                                              // mean, or mean + var / 2, of the valid logits
+    const float cnt = (float)(min(lim, kLeaf - 1) + 1);
+    float s1 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s1 += key_off(mt, r) <= lim ? acc[mt][r] : 0.f;
+    s1 = wave_add_xor(s1, 16);
+    s1 = wave_add_xor(s1, 32);
+    const float mean = s1 / cnt;                        // of the raw dot products
+    head = mean * a.scale;
+    if (a.score == 2) {
+      float s2 = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dv = (acc[mt][r] - mean) * a.scale;
+          s2 += key_off(mt, r) <= lim ? dv * dv : 0.f;
+        }
+      s2 = wave_add_xor(s2, 16);
+      s2 = wave_add_xor(s2, 32);
+      head += 0.5f * s2 / cnt;
+    }
   }
-  float m = kNegInf;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][r]);
-  m = wave_max_xor(m, 16);
-  m = wave_max_xor(m, 32);
-  const float mc = m * c2;
-  float s = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
-  s = wave_add_xor(s, 16);
-  s = wave_add_xor(s, 32);
-  // natural-log LSE of this head: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
-  const float u = row_sum_to_last(head_ok ? (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f : 0.f);
+  const float u = row_sum_to_last(head_ok ? head : 0.f);
   if (lane == 15) uout[(int64_t)t * a.width + slot] = u;   // the group's head sum (row 0)
 }
 

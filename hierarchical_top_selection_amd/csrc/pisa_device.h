@@ -165,6 +165,25 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// ----------------------------------------------------------------------------- candidate scores
+// Score of a candidate from the raw dot products y0, y1 of its two children (valid where ok0 /
+// ok1), "Block Sparse Attention with Log-Linear Complexity", Core method: mode 0 is the LSE of
+// eq. 21, returned in base-2 units (logits y * c2, c2 = scale * log2 e); modes 1 and 2 are its
+// first- and second-order Taylor truncations (PISA-1 / PISA-2): the mean, and the mean plus half
+// the population variance, of the logits y * scale, in natural units.  -inf without a valid child.
+__device__ inline float pair_score(float y0, float y1, bool ok0, bool ok1, int mode, float scale, float c2) {
+  if (mode == 0) {
+    const float z0 = ok0 ? y0 * c2 : kNegInf, z1 = ok1 ? y1 * c2 : kNegInf;
+    const float m = fmaxf(z0, z1);
+    return m == kNegInf ? kNegInf : m + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(z0, z1) - m));
+  }
+  if (!(ok0 || ok1)) return kNegInf;
+  const float a = y0 * scale, b = y1 * scale;
+  if (!(ok0 && ok1)) return ok0 ? a : b;
+  const float mean = 0.5f * (a + b), h = 0.5f * (a - b);
+  return mode == 2 ? mean + 0.5f * h * h : mean;
+}
+
 // Index of the p-th set bit (p counted from 0) of a non-empty 64-bit mask.
 __device__ inline int nth_set_bit(uint64_t mask, int p) {
   int pos = 0;

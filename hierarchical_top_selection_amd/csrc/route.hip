@@ -21,7 +21,8 @@
 // 32 fp32 MFMAs per tile, from the same 4 bytes per element.  The kernel
 // gathers summary rows (8 KB per 16-child tile), so each tile's rows are
 // requested one tile ahead.  The LSE of a candidate's two children is evaluated
-// in base 2 as max + log2(1 + 2^-|diff|) on pre-scaled logits.
+// in base 2 as max + log2(1 + 2^-|diff|) on pre-scaled logits; the mean and mean + var/2 score
+// variants (PISA-1 / PISA-2) from the same two logits in natural units.
 #include "kernels.h"
 
 namespace pisa {
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
 }
 
 // ----------------------------------------------------------------------------- routing
-template <typename T, int D>
+// kScore: the candidate score (pisa_score), fixed per instantiation so only its code is live.
+template <typename T, int D, int kScore>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -181,21 +183,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         }
         // S^T tile: rows = 16 children, columns = heads; lane (g, col) gets children 4g + i of head col
         const floatx4 acc = Ops::dot(kf, qf);
-        float pair_score[2];
+        float pscore[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {                  // candidate 8 nt + 2g + h: children rows 4g + 2h, +1
           const int r0 = 4 * g + 2 * h;
-          const float z0 = ((okmask >> r0) & 1) ? acc[2 * h] * c2 : kNegInf;
-          const float z1 = ((okmask >> (r0 + 1)) & 1) ? acc[2 * h + 1] * c2 : kNegInf;
-          const float m = fmaxf(z0, z1);
-          const float sc = m == kNegInf ? kNegInf
-                                        : m + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(z0, z1) - m));
-          pair_score[h] = row_sum_to_last(col < a.group ? sc : 0.f);   // sum over the group's heads
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], (okmask >> r0) & 1, (okmask >> (r0 + 1)) & 1,
+                                      kScore, a.scale, c2);
+          pscore[h] = row_sum_to_last(col < a.group ? sc : 0.f);   // sum over the group's heads
         }
         // lane 16 g + 15 holds candidates 8 nt + 2 g and 8 nt + 2 g + 1
         const int src = 16 * ((lane & 7) >> 1) + 15;
-        const float s0 = __shfl(pair_score[0], src, 64);
-        const float s1 = __shfl(pair_score[1], src, 64);
+        const float s0 = __shfl(pscore[0], src, 64);
+        const float s1 = __shfl(pscore[1], src, 64);
         if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
       }
       // exact rank among the candidates; lane j's values are read into scalar registers
@@ -222,7 +221,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
-  hipLaunchKernelGGL((route_kernel<T, D>), grid, dim3(256), 0, s, a);
+  if (a.score == 1)
+    hipLaunchKernelGGL((route_kernel<T, D, 1>), grid, dim3(256), 0, s, a);
+  else if (a.score == 2)
+    hipLaunchKernelGGL((route_kernel<T, D, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((route_kernel<T, D, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

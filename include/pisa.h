@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 2
+#define PISA_ABI_VERSION 3
 
 typedef enum {
   PISA_OK = 0,
@@ -66,6 +66,15 @@ typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
  * seq_len * 2 * top_k < 2^31.  scale <= 0 selects 1/sqrt(head_dim), the scale
  * of the LSE score (Core method, eq. 21), also used by attention.
  */
+/* Candidate score from the logits of a candidate's valid children (raw keys <= t
+ * at the leaf level).  PISA_SCORE_LSE is the method's log-sum-exp (Core method
+ * eq. 21); PISA_SCORE_MEAN and PISA_SCORE_MEAN_VAR are its first- and
+ * second-order truncations from the Taylor expansion of the LSE (Core method; the
+ * PISA-1 and PISA-2 variants): the mean, and the mean plus half the population
+ * variance, of the valid children's logits, without the log(count) term.  Scores
+ * are summed over the group's query heads in every case. */
+typedef enum { PISA_SCORE_LSE = 0, PISA_SCORE_MEAN = 1, PISA_SCORE_MEAN_VAR = 2 } pisa_score;
+
 typedef struct {
   int32_t batch;        /* B */
   int32_t seq_len;      /* N for prefill; KV-cache capacity for decode */
@@ -77,6 +86,7 @@ typedef struct {
   int32_t top_k;        /* K, leaf blocks kept per (token, KV head) */
   pisa_dtype dtype;     /* element type of Q, K, V, O and the KV caches */
   float scale;          /* logit scale; <= 0 means 1/sqrt(head_dim) */
+  pisa_score score;     /* candidate score at every level (routing, leaves, decode) */
 } pisa_cfg;
 
 typedef struct { const void* ptr; int64_t stride_b, stride_t, stride_h; } pisa_tensor;

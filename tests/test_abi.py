@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(declared) == 13
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 2
+    assert lib.pisa_abi_version() == 3
 
 
 def test_status_strings(lib):
