@@ -206,6 +206,35 @@ def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
     return out
 
 
+def variant_selection(q, k, n_kv_heads: int, K: int, reps: int = 5) -> dict:
+    """Selection latency (pyramid + select_blocks) of each candidate score on one input, median of reps."""
+    import torch
+
+    from hierarchical_top_selection_amd import binding
+
+    B, N, Hq, d = q.shape
+    cfg = binding.make_cfg(B, N, Hq, n_kv_heads, d, K, q.dtype)
+    ws = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    pyr = torch.empty((B, n_kv_heads, binding.pyramid_nodes(N), d), dtype=torch.float32, device=q.device)
+    sel = torch.empty((B, n_kv_heads, N, K), dtype=torch.int32, device=q.device)
+    out = {"K": K}
+    for score in ("lse", "mean", "mean_var"):
+        def fn():
+            binding.build_pyramid(k, out=pyr)
+            binding.select_blocks(q, k, pyr, K, workspace=ws, out=sel, score=score)
+        fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out[f"{score}_select_ms"] = sorted(times)[len(times) // 2]
+    return out
+
+
 def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
     """Decode throughput: `decode_steps` steps of every sequence after a prebuilt context.
 
@@ -319,6 +348,7 @@ def main() -> int:
     if not args.no_sweep:
         q_main, k_main = _INPUTS[w.name]
         extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
+        extra["score_variants"] = variant_selection(q_main, k_main, w.n_kv_heads, w.top_k)
     _INPUTS.clear()
     if not args.no_decode:
         extra["decode_b64_ctx131072"] = run_decode(W.WORKLOADS["decode_b64_ctx131072"])
