@@ -235,6 +235,48 @@ def variant_selection(q, k, n_kv_heads: int, K: int, reps: int = 5) -> dict:
     return out
 
 
+def _mean_present(xs):
+    xs = [x for x in xs if x is not None]
+    return sum(xs) / len(xs) if xs else None
+
+
+def selection_quality(q, k, n_kv_heads: int, K: int, tokens: int = 256, seed: int = 5) -> dict:
+    """Recall@K against the exact flat top-K and retained attention mass of each selector.
+
+    The hierarchical selection with each candidate score and the flat mean-key scan select
+    on the full input; `quality.selection_quality` then scores `tokens` sampled positions
+    t >= 2 K C (where a choice exists) against the exact per-leaf LSE, spread over the
+    KV heads.  Not timed: a measurement of what is selected, reported beside the speed.
+    """
+    import numpy as np
+    import torch
+
+    from hierarchical_top_selection_amd import binding, quality
+
+    B, N, Hq, d = q.shape
+    pyr = binding.build_pyramid(k)
+    sels = {f"pisa_{score}": binding.select_blocks(q, k, pyr, K, score=score) for score in ("lse", "mean", "mean_var")}
+    sels["flat_mean"] = binding.select_flat(q, pyr, n_kv_heads, K)
+    torch.cuda.synchronize()
+    heads = min(n_kv_heads, 4)
+    rng = np.random.default_rng(seed)
+    acc = {}
+    for kvh in range(heads):
+        ts = np.sort(rng.choice(np.arange(2 * K * 64, N), tokens // heads, replace=False))
+        r = quality.selection_quality(q, k, sels, ts, K, kvh=kvh)
+        for name, m in r.items():
+            a = acc.setdefault(name, {key: [] for key in m})
+            for key, val in m.items():
+                a[key].append(val)
+    out = {"K": K, "tokens": (tokens // heads) * heads, "kv_heads": heads, "position_bins": 4}
+    for name, a in acc.items():
+        out[name] = {"recall": float(np.mean(a["recall"])), "mass": float(np.mean(a["mass"])),
+                     **{key: [_mean_present([x[i] for x in a[key]]) for i in range(4)]
+                        for key in ("recall_by_position", "mass_by_position")}}
+    del sels, pyr
+    return out
+
+
 def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
     """Decode throughput: `decode_steps` steps of every sequence after a prebuilt context.
 
@@ -313,6 +355,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing record")
+    ap.add_argument("--no-quality", action="store_true", help="skip the selection-quality record")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the hierarchical vs single-level selection sweep (K = 8, N = 4K .. the workload's N)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -349,6 +392,14 @@ def main() -> int:
         q_main, k_main = _INPUTS[w.name]
         extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
         extra["score_variants"] = variant_selection(q_main, k_main, w.n_kv_heads, w.top_k)
+    if not args.no_quality:
+        q_main, k_main = _INPUTS[w.name]
+        extra["selection_quality_k8"] = selection_quality(q_main, k_main, w.n_kv_heads, 8)
+        for name in ("quality_diffuse_n65536", "quality_needles_n65536", "quality_runs_n65536"):
+            rw = W.WORKLOADS[name]
+            rq, rk, _ = _device_inputs(rw)
+            extra[name] = selection_quality(rq, rk, rw.n_kv_heads, rw.top_k)
+            del rq, rk
     _INPUTS.clear()
     if not args.no_decode:
         extra["decode_b64_ctx131072"] = run_decode(W.WORKLOADS["decode_b64_ctx131072"])

@@ -7,7 +7,9 @@ bytes.
 
 Shapes and value distributions follow the five workloads the path is
 measured on (tiny fp32 prefill, 4K / 32K / 256K bf16 prefill, and a
-64-sequence decode over a 131072-token context).  The pages that describe
+64-sequence decode over a 131072-token context), plus three 64K input
+regimes of the selection-quality study (diffuse, isolated strong blocks, and
+strong blocks in runs of adjacent leaves).  The pages that describe
 PISA measure selection on real model activations, which are not available
 here; these planted Gaussian inputs stand in for them.
 
@@ -17,7 +19,9 @@ Recipe (every draw is ``numpy.random.default_rng([seed, tensor_id, ...])``):
 * ``Q[b, :, h, :]``   = ``rng([seed, 0, b, h]).standard_normal((N, d))`` + alpha_q * u
 * ``K[b, :, kvh, :]`` = ``rng([seed, 1, b, kvh]).standard_normal((N, d))``, plus
   alpha_k * u on every key of ``n_plant`` leaf blocks chosen by
-  ``rng([seed, 98, b, kvh]).choice(M1, n_plant, replace=False)``.
+  ``rng([seed, 98, b, kvh]).choice(M1, n_plant, replace=False)``; with
+  ``plant_run`` = r > 1 the same stream instead picks ceil(n_plant / r) of the
+  aligned runs of r adjacent leaves.
 * ``V[b, :, kvh, :]`` = ``rng([seed, 2, b, kvh]).standard_normal((N, d))``
 * decode tokens: ``rng([seed, 10|11|12, b, head]).standard_normal((steps, d))``
   for q / k_new / v_new.
@@ -52,6 +56,7 @@ class Workload:
     decode_steps: int = 0
     block: int = LEAF
     fanout: int = FANOUT
+    plant_run: int = 1    # planted blocks come in runs of this many adjacent leaves
 
     @property
     def group(self) -> int:
@@ -83,6 +88,16 @@ WORKLOADS = {
     "prefill_n262144": Workload("prefill_n262144", seed=3, batch=1, seq_len=262144, head_dim=128,
                                 n_q_heads=16, n_kv_heads=1, top_k=16, dtype="bf16",
                                 plant_blocks=_plant_count(0.005, 4096), alpha_k=2.5, alpha_q=1.0),
+    # input regimes of the selection-quality study (64K tokens, one KV group, K = 8)
+    "quality_diffuse_n65536": Workload("quality_diffuse_n65536", seed=21, batch=1, seq_len=65536, head_dim=128,
+                                       n_q_heads=16, n_kv_heads=1, top_k=8, dtype="bf16",
+                                       plant_blocks=_plant_count(0.005, 1024), alpha_k=2.5, alpha_q=1.0),
+    "quality_needles_n65536": Workload("quality_needles_n65536", seed=22, batch=1, seq_len=65536, head_dim=128,
+                                       n_q_heads=16, n_kv_heads=1, top_k=8, dtype="bf16",
+                                       plant_blocks=_plant_count(0.01, 1024), alpha_k=12.0, alpha_q=2.0),
+    "quality_runs_n65536": Workload("quality_runs_n65536", seed=23, batch=1, seq_len=65536, head_dim=128,
+                                    n_q_heads=16, n_kv_heads=1, top_k=8, dtype="bf16",
+                                    plant_blocks=_plant_count(0.01, 1024), alpha_k=12.0, alpha_q=2.0, plant_run=8),
     "decode_b64_ctx131072": Workload("decode_b64_ctx131072", seed=4, batch=64, seq_len=131072,
                                      head_dim=128, n_q_heads=32, n_kv_heads=8, top_k=16,
                                      dtype="bf16", plant_blocks=0, alpha_k=0.0, alpha_q=0.0,
@@ -124,7 +139,11 @@ def planted_blocks(w: Workload, b: int, kvh: int, n_leaves: int | None = None) -
     m1 = w.n_leaves if n_leaves is None else n_leaves
     if w.plant_blocks <= 0:
         return np.zeros(0, dtype=np.int64)
-    return np.sort(_rng(w.seed, 98, b, kvh).choice(m1, min(w.plant_blocks, m1), replace=False))
+    if w.plant_run <= 1:
+        return np.sort(_rng(w.seed, 98, b, kvh).choice(m1, min(w.plant_blocks, m1), replace=False))
+    runs = m1 // w.plant_run                    # run r covers leaves [r * run, (r + 1) * run)
+    pick = _rng(w.seed, 98, b, kvh).choice(runs, min(-(-w.plant_blocks // w.plant_run), runs), replace=False)
+    return np.sort((pick[:, None] * w.plant_run + np.arange(w.plant_run)[None, :]).ravel())
 
 
 def _draw_q(w: Workload, b: int, h: int, n: int) -> np.ndarray:
