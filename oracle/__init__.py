@@ -29,6 +29,13 @@ framework (every valid leaf scored by its mean-key dot product, head sum,
 top K); it is pinned to the exact-LSE brute force through the closed forms
 of constant-key blocks and of the small-logit limit.
 
+``pisa.attention_backward`` gives the gradients of the block-sparse attention
+with the selections held fixed (the page calls the method trainable but
+states no gradient); it is pinned by central finite differences of the
+forward oracle, by float64 autograd of dense causal attention when every
+leaf is selected, and by the softmax-gradient invariants (sum of dk = 0,
+sum of dv = sum of dO).
+
 Parity status
 -------------
 Pinned: pyramid (closed form over full spans, hand-derived partial-node

@@ -43,6 +43,12 @@ Readings where the pages are silent (each listed in the design notes):
       of the pyramid (built over the whole block, like every summary), sums
       the scores over the group's heads [Prereq/GQA] and keeps K by
       (score desc, index asc).
+  R9  Gradients [Steps, attention on the selected leaves; the page calls the
+      method trainable but gives no gradient treatment]: the gradient of the
+      block-sparse attention output with the selected sets held fixed (the
+      selection is piecewise constant in q and k, so no gradient flows
+      through it).  Only the attention's dependence on q, k and v is
+      differentiated; the routing scores carry none.
 """
 from __future__ import annotations
 
@@ -351,6 +357,46 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, ts: 
     p = np.exp(logits - lse[..., None])
     o = np.matmul(p, v[pos])                                                      # [T, G, d]
     return o, lse, p.sum(axis=-1)
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, ts: np.ndarray,
+                       do: np.ndarray, C: int = 64, scale: float | None = None):
+    """Gradients of `attention` for one (b, kvh) slice with the selections held fixed (R9).
+
+    For each token t and head h with logits s = scale q . k_r over the keys r of its
+    selected blocks (cut to r <= t), P = softmax(s), O = P V and upstream gradient dO:
+      dV_r += P_r dO,   dP_r = dO . v_r,   Delta = sum_r P_r dP_r (= dO . O),
+      dS_r = P_r (dP_r - Delta),   dq = scale sum_r dS_r k_r,   dk_r += scale dS_r q.
+    Tokens are the rows ts of q / do; keys that several tokens select collect every
+    token's contribution.  Returns (dq [T, G, d], dk [n, d], dv [n, d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    ts = np.asarray(ts, dtype=np.int64)
+    T, G, d = q.shape
+    n = k.shape[0]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r in range(T):
+        t = int(ts[r])
+        blocks = [int(j) for j in sel[r] if j >= 0]
+        pos = np.array([p for j in blocks for p in range(j * C, min((j + 1) * C, n)) if p <= t], dtype=np.int64)
+        if pos.size == 0:
+            continue
+        kr, vr = k[pos], v[pos]                                     # [m, d]
+        s = (q[r] @ kr.T) * scale                                   # [G, m]
+        p = np.exp(s - logsumexp(s, axis=-1)[:, None])
+        dp = do[r] @ vr.T                                           # [G, m]
+        delta = (p * dp).sum(axis=-1, keepdims=True)
+        ds = p * (dp - delta)
+        dq[r] = scale * (ds @ kr)
+        np.add.at(dk, pos, scale * (ds.T @ q[r]))
+        np.add.at(dv, pos, p.T @ do[r])
+    return dq, dk, dv
 
 
 def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, ts: np.ndarray,

@@ -404,3 +404,82 @@ def test_mean_score_without_cuts_equals_the_flat_mean_selection():
     for r in range(len(ts)):
         if gap[r] > 1e-9:
             assert list(sel[r]) == list(flat[r]), ts[r]
+
+
+# ----------------------------------------------------------------------------- gradients (R9)
+def _bwd_case(seed, n=150, G=2, d=4, K=2, C=16):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, G, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    do = rng.standard_normal((n, G, d))
+    ts = np.arange(n)
+    sel, _ = pisa.route(q, k, pisa.build_pyramid(k, C), ts, K, C=C)
+    return q, k, v, do, ts, sel, C
+
+
+def test_attention_backward_matches_finite_differences():
+    """R9: dq, dk, dv are the derivatives of L = sum(dO * O) with the selections held fixed;
+    central differences of the forward oracle (fp64, step 1e-6) on every coordinate."""
+    q, k, v, do, ts, sel, C = _bwd_case(0, n=40, G=2, d=3, K=1, C=8)
+    dq, dk, dv = pisa.attention_backward(q, k, v, sel, ts, do, C=C)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(pisa.attention(qq, kk, vv, sel, ts, C=C)[0] * do))
+
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            ap = [xp if a is x else a for a in args]
+            am = [xm if a is x else a for a in args]
+            num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_attention_backward_dense_equals_autograd_of_textbook_attention():
+    """With every leaf selected the sparse attention is dense causal attention, so its gradients are
+    torch float64 autograd of the textbook form softmax(q k^T scale + causal mask) v."""
+    import torch
+
+    n, G, d, C = 90, 3, 5, 16
+    rng = np.random.default_rng(1)
+    q, k, v, do = (rng.standard_normal(s) for s in ((n, G, d), (n, d), (n, d), (n, G, d)))
+    ts = np.arange(n)
+    m1 = -(-n // C)
+    sel = np.tile(np.arange(m1), (n, 1))
+    sel = np.where(sel * C <= ts[:, None], sel, -1)
+    dq, dk, dv = pisa.attention_backward(q, k, v, sel, ts, do, C=C)
+
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    logits = torch.einsum("tgd,sd->tgs", qt, kt) / math.sqrt(d)
+    mask = torch.arange(n)[None, :] > torch.arange(n)[:, None]
+    logits = logits.masked_fill(mask[:, None, :], float("-inf"))
+    out = torch.einsum("tgs,sd->tgd", torch.softmax(logits, dim=-1), vt)
+    out.backward(torch.tensor(do))
+    for got, want in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_backward_invariants(seed):
+    """Closed forms of the softmax gradient: each row's dS sums to zero, so sum_r dk_r = 0; each row's
+    weights sum to one, so sum_r dv_r = sum over tokens and heads of dO; rows with no key get dq = 0."""
+    q, k, v, do, ts, sel, C = _bwd_case(10 + seed)
+    dq, dk, dv = pisa.attention_backward(q, k, v, sel, ts, do, C=C)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-10)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=(0, 1)), rtol=1e-10, atol=1e-10)
+    sel_none = sel.copy()
+    sel_none[5] = -1
+    dq2, _, _ = pisa.attention_backward(q, k, v, sel_none, ts, do, C=C)
+    assert np.all(dq2[5] == 0.0)
+    # keys no token selects get no gradient
+    used = np.zeros(k.shape[0], dtype=bool)
+    for r, t in enumerate(ts):
+        for j in sel[r][sel[r] >= 0]:
+            used[j * C:min((j + 1) * C, t + 1)] = True
+    assert np.all(dk[~used] == 0.0) and np.all(dv[~used] == 0.0)
