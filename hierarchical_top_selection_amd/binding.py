@@ -62,6 +62,11 @@ _SIGNATURES = {
     "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
                                             PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
+    "pisa_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
+    "pisa_sparse_attn_bwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
+                                            PisaTensor, PisaTensor, ctypes.c_int, ctypes.c_void_p, PisaTensor,
+                                            PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
     "pisa_decode_step": (ctypes.c_int, [_P(PisaCfg), ctypes.c_int32, PisaTensor, PisaTensor, PisaTensor,
                                         PisaTensor, PisaTensor, ctypes.c_void_p, ctypes.c_void_p, PisaTensor,
                                         ctypes.c_int, ctypes.c_void_p]),
@@ -235,6 +240,44 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
         _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
         ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_len), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def attn_bwd_workspace_bytes(cfg: PisaCfg) -> int:
+    return int(lib().pisa_attn_bwd_workspace_bytes(ctypes.byref(cfg)))
+
+
+def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, o: torch.Tensor,
+                    row_lse: torch.Tensor, dout: torch.Tensor, scale: float = 0.0, workspace: torch.Tensor | None = None,
+                    dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Gradients (dq [B, N, Hq, d], dk and dv [B, N, Hkv, d], float32) of `sparse_attn_fwd` with the
+    selections held fixed; o and row_lse are that call's output and row LSE, dout the upstream
+    gradient (same dtype as o)."""
+    B, N, Hq, d = q.shape
+    top_k = sel.shape[-1]
+    cfg = _cfg_from(q, k, top_k, scale)
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, k.shape[2], N, top_k):
+        raise ValueError("selection must be a contiguous int32 [B, Hkv, N, K] tensor")
+    if dout.dtype != o.dtype or dout.shape != o.shape or o.shape != q.shape:
+        raise ValueError("o and dout must have q's shape and one dtype")
+    if row_lse.dtype != torch.float32 or not row_lse.is_contiguous() or row_lse.shape != (B, Hq, N):
+        raise ValueError("row_lse must be a contiguous float32 [B, Hq, N] tensor")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(k.shape, **f32) if dk is None else dk
+    dv = torch.empty(v.shape, **f32) if dv is None else dv
+    for x in (dq, dk, dv):
+        if x.dtype != torch.float32:
+            raise ValueError("gradients are float32")
+    need = attn_bwd_workspace_bytes(cfg)
+    if need == 0:
+        raise RuntimeError("pisa_sparse_attn_bwd: unsupported configuration")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("pisa_sparse_attn_bwd", lib().pisa_sparse_attn_bwd(
+        ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()), _tensor(o),
+        _tensor(dout), _dtype_code(dout), ctypes.c_void_p(row_lse.data_ptr()), _tensor(dq), _tensor(dk), _tensor(dv),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return dq, dk, dv
 
 
 def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,

@@ -124,6 +124,47 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   return w;
 }
 
+struct BwdWorkspace {
+  size_t kpack, vrows, kcols, stats, rank, hist, seg_len, seg_base, item_base, list, items, n_items, partial, total;
+  int64_t max_items;
+};
+
+// Backward workspace: three packed copies of K / V, the row statistics, the inverse index of
+// the selections and the per-item dK / dV partial sums (see BwdArgs).
+BwdWorkspace bwd_layout(const pisa_cfg* c) {
+  BwdWorkspace w;
+  const int64_t bh = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t m1 = (c->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
+  const int64_t chunks = (c->seq_len + pisa::kBwdChunk - 1) / pisa::kBwdChunk;
+  const int64_t slots = bh * c->seq_len * c->top_k;
+  const size_t pack = (size_t)bh * m1 * pisa::kLeaf * c->head_dim * 2;
+  w.max_items = slots / pisa::kBwdItem + bh * m1;         // sum over blocks of ceil(len / 512)
+  w.kpack = 0;
+  w.vrows = align256(w.kpack + pack);
+  w.kcols = align256(w.vrows + pack);
+  w.stats = align256(w.kcols + pack);
+  w.rank = align256(w.stats + (size_t)bh * c->seq_len * 16 * 8);
+  w.hist = align256(w.rank + (size_t)slots * 4);
+  w.seg_len = align256(w.hist + (size_t)bh * chunks * m1 * 4);
+  w.seg_base = align256(w.seg_len + (size_t)bh * m1 * 4);
+  w.item_base = align256(w.seg_base + (size_t)bh * m1 * 4);
+  w.list = align256(w.item_base + (size_t)bh * m1 * 4);
+  w.items = align256(w.list + (size_t)slots * 4);
+  w.n_items = align256(w.items + (size_t)w.max_items * 8);
+  w.partial = align256(w.n_items + 4);
+  w.total = align256(w.partial + (size_t)w.max_items * 2 * pisa::kLeaf * c->head_dim * 4);
+  return w;
+}
+
+pisa_status check_bwd_cfg(const pisa_cfg* c) {
+  pisa_status st = check_cfg(c);
+  if (st != PISA_OK) return st;
+  if (c->dtype != PISA_BF16) return PISA_ERR_UNSUPPORTED;
+  if ((c->seq_len + pisa::kLeaf - 1) / pisa::kLeaf > pisa::kBwdMaxLeaves) return PISA_ERR_UNSUPPORTED;
+  if ((int64_t)c->batch * c->n_kv_heads * c->seq_len * c->top_k > INT32_MAX) return PISA_ERR_UNSUPPORTED;
+  return PISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,6 +353,61 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
   a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = o_dtype == PISA_BF16;
   return hip_status(pisa::launch_attention(a, (hipStream_t)stream));
+}
+
+size_t pisa_attn_bwd_workspace_bytes(const pisa_cfg* cfg) {
+  if (check_bwd_cfg(cfg) != PISA_OK) return 0;
+  return bwd_layout(cfg).total;
+}
+
+pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, pisa_dtype grad_dtype,
+                                 const float* row_lse, pisa_tensor_mut dq, pisa_tensor_mut dk, pisa_tensor_mut dv,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  pisa_status st = check_bwd_cfg(cfg);
+  if (st != PISA_OK) return st;
+  const BwdWorkspace w = bwd_layout(cfg);
+  if (!ws || ws_bytes < w.total || ((uintptr_t)ws & 255u)) return PISA_ERR_WORKSPACE;
+  if (grad_dtype != PISA_F32 && grad_dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
+  if ((st = check_tensor(q.ptr, q.stride_b, q.stride_t, q.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(k.ptr, k.stride_b, k.stride_t, k.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(v.ptr, v.stride_b, v.stride_t, v.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(o.ptr, o.stride_b, o.stride_t, o.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(dout.ptr, dout.stride_b, dout.stride_t, dout.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(dq.ptr, dq.stride_b, dq.stride_t, dq.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(dk.ptr, dk.stride_b, dk.stride_t, dk.stride_h)) != PISA_OK) return st;
+  if ((st = check_tensor(dv.ptr, dv.stride_b, dv.stride_t, dv.stride_h)) != PISA_OK) return st;
+  if (!sel || !row_lse) return PISA_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(ws);
+  pisa::BwdArgs a;
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_st = q.stride_t; a.q_sh = q.stride_h;
+  a.k = k.ptr; a.k_sb = k.stride_b; a.k_st = k.stride_t; a.k_sh = k.stride_h;
+  a.v = v.ptr; a.v_sb = v.stride_b; a.v_st = v.stride_t; a.v_sh = v.stride_h;
+  a.sel = sel;
+  a.o = o.ptr; a.o_sb = o.stride_b; a.o_st = o.stride_t; a.o_sh = o.stride_h;
+  a.dout = dout.ptr; a.do_sb = dout.stride_b; a.do_st = dout.stride_t; a.do_sh = dout.stride_h;
+  a.row_lse = row_lse;
+  a.dq = static_cast<float*>(dq.ptr); a.dq_sb = dq.stride_b; a.dq_st = dq.stride_t; a.dq_sh = dq.stride_h;
+  a.dk = static_cast<float*>(dk.ptr); a.dk_sb = dk.stride_b; a.dk_st = dk.stride_t; a.dk_sh = dk.stride_h;
+  a.dv = static_cast<float*>(dv.ptr); a.dv_sb = dv.stride_b; a.dv_st = dv.stride_t; a.dv_sh = dv.stride_h;
+  a.kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
+  a.vrows = reinterpret_cast<pisa::bf16x8*>(base + w.vrows);
+  a.kcols = reinterpret_cast<pisa::bf16x8*>(base + w.kcols);
+  a.stats = reinterpret_cast<float2*>(base + w.stats);
+  a.rank = reinterpret_cast<int32_t*>(base + w.rank);
+  a.hist = reinterpret_cast<int32_t*>(base + w.hist);
+  a.seg_len = reinterpret_cast<int32_t*>(base + w.seg_len);
+  a.seg_base = reinterpret_cast<int32_t*>(base + w.seg_base);
+  a.item_base = reinterpret_cast<int32_t*>(base + w.item_base);
+  a.list = reinterpret_cast<int32_t*>(base + w.list);
+  a.items = reinterpret_cast<int2*>(base + w.items);
+  a.n_items = reinterpret_cast<int32_t*>(base + w.n_items);
+  a.partial = reinterpret_cast<float*>(base + w.partial);
+  a.max_items = w.max_items;
+  a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
+  a.scale = resolve_scale(cfg); a.grad_bf16 = grad_dtype == PISA_BF16;
+  return hip_status(pisa::launch_attention_bwd(a, (hipStream_t)stream));
 }
 
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,

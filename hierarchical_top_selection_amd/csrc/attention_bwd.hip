@@ -1,0 +1,492 @@
+// attention_bwd.hip - gradients of the block-sparse attention of "Block Sparse Attention
+// with Log-Linear Complexity" (Prerequisites, block sparse attention; Method steps,
+// fourth step) with the selected sets held fixed.  The page calls the method trainable but
+// states no gradient; the selection is piecewise constant in q and k, so only the
+// attention over the selected keys is differentiated.  For token t, head h and key r of
+// its selected blocks (r <= t), with P = softmax(scale q . k_r) and upstream dO:
+//   dV_r += P_r dO,  dP_r = dO . v_r,  Delta = dO . O,  dS_r = P_r (dP_r - Delta),
+//   dq = scale sum_r dS_r k_r,  dk_r += scale dS_r q.
+//
+// Two passes over the (token, block) pairs, both bf16 MFMA with fp32 accumulation:
+//
+// * dq, query-major: one wave per (b, kvh, token), the group's heads as the 16 MFMA
+//   columns, exactly the shape of the forward kernel.  Per selected block it forms
+//   S^T = K Q^T and dP^T = V dO^T from packed key-major rows, rescales with the saved row
+//   LSE (no online softmax: P is final), and accumulates dq^T += K^T dS^T from K packed in
+//   the value layout, so the lane's own dS^T values are the B fragment.
+// * dk and dv, key-major: a deterministic inverse of the selection lists each block's
+//   tokens in ascending order (a stable counting sort: per-chunk occurrence ranks, a
+//   per-block scan over chunks, one scan over blocks, a scatter).  A work item is up to
+//   512 tokens of one block; its four waves own 16 keys each, stage the tokens' queries
+//   and output gradients in LDS (row-major and transposed), form S = Q K^T and dP = dO V^T
+//   with the heads as rows, and accumulate dv^T += dO^T P and dk^T += Q^T dS on the
+//   16x16x16 MFMA, whose contraction runs over the 16 head rows.  Items write partial
+//   sums; a last pass adds each block's partials in item order.  No atomics anywhere, so
+//   repeated calls give identical bits.
+#include "kernels.h"
+
+namespace pisa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline floatx4 mfma_k16(bf16x4 a, bf16x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Eight consecutive gradient elements as bf16 (p 16-byte aligned for bf16, 32-byte for f32).
+__device__ inline bf16x8 load8_bf16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ inline bf16x8 load8_bf16(const float* p) {
+  const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
+  bf16x8 r;
+  r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
+  r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
+  return r;
+}
+
+// Lane < K holds slot `lane` of the token's selection; true for entries that take part:
+// a block j with 0 <= j <= t / 64 not listed in an earlier slot.  Called by the whole wave.
+__device__ inline bool slot_in_use(int j, int lane, int K, int t) {
+  bool ok = lane < K && j >= 0 && j <= t / kLeaf;
+  for (int e = 0; e < K; ++e) {
+    const int je = __shfl(j, e, 64);
+    if (e < lane && je == j) ok = false;
+  }
+  return ok;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- row statistics
+// stats[bh][t][h] = (row LSE * log2 e, Delta = dO . O) for the group's heads; +inf / 0 for
+// the padding columns h >= G, which makes their probabilities exactly zero.
+template <typename TD>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n) return;
+  const int bh = blockIdx.y, b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int g = lane >> 4, col = lane & 15;
+  const int quarter = a.head_dim / 4;
+  float acc = 0.f;
+  if (col < a.group) {
+    const int head = kvh * a.group + col;
+    const TD* orow = reinterpret_cast<const TD*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh +
+                     g * quarter;
+    const TD* drow = reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
+                     (int64_t)head * a.do_sh + g * quarter;
+    for (int i = 0; i < quarter; i += 4) {
+      const float4 x = load4(orow + i), y = load4(drow + i);
+      acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
+  }
+  acc = wave_add_xor(acc, 16);
+  acc = wave_add_xor(acc, 32);
+  if (g == 0) {
+    float2 st = make_float2(__builtin_huge_valf(), 0.f);
+    if (col < a.group) {
+      const int hq = a.n_kv_heads * a.group;
+      st.x = a.row_lse[((int64_t)b * hq + kvh * a.group + col) * a.n + t] * kLog2e;
+      st.y = acc;
+    }
+    a.stats[((int64_t)bh * a.n + t) * 16 + col] = st;
+  }
+}
+
+// ----------------------------------------------------------------------------- inverse index
+// Chunk c of 256 tokens of (b, kvh): rank[t][s] = how many earlier tokens of the chunk list
+// the block of slot s (-1 for slots not in use); hist[c][j] = the chunk's count of block j.
+// Counting runs in token order in one wave, so ranks are deterministic.
+__global__ __launch_bounds__(256) void bwd_rank_kernel(BwdArgs a, int chunks) {
+  extern __shared__ int32_t lds[];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int K = a.top_k;
+  const int t0 = c * kBwdChunk;
+  const int nt = min(kBwdChunk, a.n - t0);
+  const int jn = (t0 + nt - 1) / kLeaf + 1;              // blocks this chunk's tokens may list
+  int32_t* sl = lds;
+  int32_t* cnt = lds + kBwdChunk * K;
+  const int32_t* src = a.sel + ((int64_t)bh * a.n + t0) * K;
+  for (int i = threadIdx.x; i < nt * K; i += blockDim.x) sl[i] = src[i];
+  for (int i = threadIdx.x; i < jn; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int i = 0; i < nt; ++i) {
+      const int t = t0 + i;
+      const int j = lane < K ? sl[i * K + lane] : -1;
+      const bool ok = slot_in_use(j, lane, K, t);
+      int r = -1;
+      if (ok) {                                           // distinct blocks: no two lanes collide
+        r = cnt[j];
+        cnt[j] = r + 1;
+      }
+      if (lane < K) a.rank[((int64_t)bh * a.n + t) * K + lane] = r;
+    }
+  }
+  __syncthreads();
+  const int m1 = ceil_div(a.n, kLeaf);
+  int32_t* h = a.hist + ((int64_t)bh * chunks + c) * m1;
+  for (int i = threadIdx.x; i < jn; i += blockDim.x) h[i] = cnt[i];
+}
+
+// Per block e = bh * M1 + j: hist[c][j] becomes the exclusive prefix over chunks (tokens of
+// earlier chunks listing j) and seg_len[e] the total.  Chunks before 64 j / 256 cannot list j.
+__global__ __launch_bounds__(256) void bwd_colscan_kernel(BwdArgs a, int chunks) {
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)a.batch * a.n_kv_heads * m1) return;
+  const int bh = (int)(e / m1), j = (int)(e % m1);
+  int32_t run = 0;
+  for (int c = j * kLeaf / kBwdChunk; c < chunks; ++c) {
+    int32_t* p = a.hist + ((int64_t)bh * chunks + c) * m1 + j;
+    const int32_t x = *p;
+    *p = run;
+    run += x;
+  }
+  a.seg_len[e] = run;
+}
+
+// One workgroup: seg_base = exclusive prefix of seg_len, item_base = exclusive prefix of the
+// items per block (ceil(seg_len / 512)), n_items = their total.
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a, int64_t blocks) {
+  __shared__ int32_t s_len[1024], s_items[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (blocks + 1023) / 1024;
+  const int64_t lo = min(blocks, (int64_t)tid * per), hi = min(blocks, lo + per);
+  int32_t sl = 0, si = 0;
+  for (int64_t e = lo; e < hi; ++e) {
+    const int32_t len = a.seg_len[e];
+    sl += len;
+    si += (len + kBwdItem - 1) / kBwdItem;
+  }
+  s_len[tid] = sl;
+  s_items[tid] = si;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {              // inclusive scan of the 1024 sums
+    const int32_t x = tid >= off ? s_len[tid - off] : 0, y = tid >= off ? s_items[tid - off] : 0;
+    __syncthreads();
+    s_len[tid] += x;
+    s_items[tid] += y;
+    __syncthreads();
+  }
+  int32_t bl = tid ? s_len[tid - 1] : 0, bi = tid ? s_items[tid - 1] : 0;
+  for (int64_t e = lo; e < hi; ++e) {
+    const int32_t len = a.seg_len[e];
+    a.seg_base[e] = bl;
+    a.item_base[e] = bi;
+    bl += len;
+    bi += (len + kBwdItem - 1) / kBwdItem;
+  }
+  if (tid == 1023) a.n_items[0] = s_items[1023];
+}
+
+// Work items of block e: (e, 512 i) for i < ceil(seg_len / 512).
+__global__ __launch_bounds__(256) void bwd_items_kernel(BwdArgs a) {
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)a.batch * a.n_kv_heads * m1) return;
+  const int32_t len = a.seg_len[e], first = a.item_base[e];
+  for (int i = 0; i * kBwdItem < len; ++i) a.items[first + i] = make_int2((int)e, i * kBwdItem);
+}
+
+// list[seg_base[e] + hist[c(t)][j] + rank] = t for every slot in use: tokens ascending per block.
+__global__ __launch_bounds__(256) void bwd_scatter_kernel(BwdArgs a, int chunks) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (bh, t)
+  if (x >= (int64_t)a.batch * a.n_kv_heads * a.n) return;
+  const int bh = (int)(x / a.n), t = (int)(x % a.n);
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int c = t / kBwdChunk;
+  for (int s = 0; s < a.top_k; ++s) {
+    const int32_t r = a.rank[x * a.top_k + s];
+    if (r < 0) continue;
+    const int j = a.sel[x * a.top_k + s];
+    const int64_t e = (int64_t)bh * m1 + j;
+    a.list[a.seg_base[e] + a.hist[((int64_t)bh * chunks + c) * m1 + j] + r] = t;
+  }
+}
+
+// ----------------------------------------------------------------------------- dq (query-major)
+template <typename TD, int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
+  typedef FragBF16<D> Frag;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n) return;
+  const int bh = blockIdx.y;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int g = lane >> 4, col = lane & 15;
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int head = kvh * a.group + col;
+
+  Frag qf, df;                                         // B fragments: head col, d k-slices
+  if (col < a.group) {
+    qf.load(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st + (int64_t)head * a.q_sh, g);
+    const TD* drow = reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
+                     (int64_t)head * a.do_sh;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) df.v[s] = load8_bf16(drow + 32 * s + 8 * g);
+  } else {
+    qf.zero();
+    df.zero();
+  }
+  const float2 st = a.stats[((int64_t)bh * a.n + t) * 16 + col];
+  const float c2 = a.scale * kLog2e;
+
+  const int64_t blk = (int64_t)bh * m1 * (kLeaf * D / 8);
+  const bf16x8* krow = a.kpack + blk + lane;
+  const bf16x8* vrow = a.vrows + blk + lane;
+  const bf16x8* kcol = a.kcols + blk + lane;
+  const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
+  uint64_t rest = __ballot(slot_in_use(my_sel, lane, a.top_k, t));
+
+  floatx4 dq[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) dq[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  while (rest) {
+    const int leaf = __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64));
+    rest &= rest - 1;
+    const int64_t first = (int64_t)leaf * kLeaf;
+    const int64_t off = (int64_t)leaf * (kLeaf * D / 8);
+    floatx4 s_acc[4], p_acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      Frag kf, vf;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        kf.v[s] = krow[off + (mt * (D / 32) + s) * 64];
+        vf.v[s] = vrow[off + (mt * (D / 32) + s) * 64];
+      }
+      s_acc[mt] = mma(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
+      p_acc[mt] = mma(vf, df, floatx4{0.f, 0.f, 0.f, 0.f});
+    }
+    // s_acc[mt][r]: key first + perm_key(mt, 4 g + r) = first + 32 (mt / 2) + 8 g + 4 (mt % 2) + r
+    const bool edge = first + kLeaf - 1 > t;
+    const int lim = (int)(t - first) - 8 * g;
+    bf16x8 db[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool masked = edge && 32 * (mt >> 1) + 4 * (mt & 1) + r > lim;
+        const float p = masked ? 0.f : exp2f(fmaf(s_acc[mt][r], c2, -st.x));
+        db[mt >> 1][4 * (mt & 1) + r] = (__bf16)(p * (p_acc[mt][r] - st.y));
+      }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      dq[dt] = mfma_bf16(kcol[off + dt * 64], db[0], dq[dt]);
+      dq[dt] = mfma_bf16(kcol[off + (D / 16 + dt) * 64], db[1], dq[dt]);
+    }
+  }
+  if (col < a.group) {
+    float* out = a.dq + b * a.dq_sb + (int64_t)t * a.dq_st + (int64_t)head * a.dq_sh;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<float4*>(out + 16 * dt + 4 * g) =
+          make_float4(dq[dt][0] * a.scale, dq[dt][1] * a.scale, dq[dt][2] * a.scale, dq[dt][3] * a.scale);
+  }
+}
+
+// ----------------------------------------------------------------------------- dk, dv (key-major)
+template <typename TD, int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
+  constexpr int kTok = 4;                 // tokens staged per round
+  constexpr int kRow = D + 8;             // padded row of the row-major copies
+  __shared__ __align__(16) __bf16 s_q[kTok][16][kRow];
+  __shared__ __align__(16) __bf16 s_do[kTok][16][kRow];
+  __shared__ __align__(16) __bf16 s_qt[kTok][D][16];
+  __shared__ __align__(16) __bf16 s_dot[kTok][D][16];
+  __shared__ float2 s_st[kTok][16];
+  __shared__ int s_tok[kTok];
+
+  const int item = blockIdx.x;
+  if (item >= a.n_items[0]) return;       // uniform over the workgroup
+  const int2 it = a.items[item];
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int e = it.x, start = it.y;
+  const int bh = e / m1, j = e % m1;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int len = min(kBwdItem, a.seg_len[e] - start);
+  const int32_t* toks = a.list + a.seg_base[e] + start;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int key = j * kLeaf + 16 * wave + col;          // this lane's key column
+
+  FragBF16<D> kb, vb;                                   // B fragments: key col, d k-slices
+  if (key < a.n) {
+    kb.load(reinterpret_cast<const __bf16*>(a.k) + b * a.k_sb + (int64_t)key * a.k_st + (int64_t)kvh * a.k_sh, g);
+    vb.load(reinterpret_cast<const __bf16*>(a.v) + b * a.v_sb + (int64_t)key * a.v_st + (int64_t)kvh * a.v_sh, g);
+  } else {
+    kb.zero();
+    vb.zero();
+  }
+  floatx4 dk[D / 16], dv[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    dk[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = a.scale * kLog2e;
+
+  for (int base = 0; base < len; base += kTok) {
+    const int nt = min(kTok, len - base);
+    for (int x = threadIdx.x; x < kTok * 16 * (D / 8); x += blockDim.x) {
+      const int tb = x / (16 * (D / 8)), rem = x % (16 * (D / 8));
+      const int h = rem / (D / 8), p = rem % (D / 8);
+      bf16x8 qv, dv8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { qv[i] = (__bf16)0.f; dv8[i] = (__bf16)0.f; }
+      if (tb < nt && h < a.group) {
+        const int t = toks[base + tb];
+        const int hd = kvh * a.group + h;
+        qv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb +
+                                              (int64_t)t * a.q_st + (int64_t)hd * a.q_sh + 8 * p);
+        dv8 = load8_bf16(reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
+                         (int64_t)hd * a.do_sh + 8 * p);
+      }
+      *reinterpret_cast<bf16x8*>(&s_q[tb][h][8 * p]) = qv;
+      *reinterpret_cast<bf16x8*>(&s_do[tb][h][8 * p]) = dv8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s_qt[tb][8 * p + i][h] = qv[i];
+        s_dot[tb][8 * p + i][h] = dv8[i];
+      }
+    }
+    if (threadIdx.x < kTok * 16) {
+      const int tb = threadIdx.x / 16, h = threadIdx.x % 16;
+      float2 st = make_float2(__builtin_huge_valf(), 0.f);
+      int t = -1;
+      if (tb < nt) {
+        t = toks[base + tb];
+        st = a.stats[((int64_t)bh * a.n + t) * 16 + h];
+      }
+      s_st[tb][h] = st;
+      if (h == 0) s_tok[tb] = t;
+    }
+    __syncthreads();
+    for (int tb = 0; tb < nt; ++tb) {
+      const int t = s_tok[tb];
+      FragBF16<D> qa, da;                               // A fragments: head col, d k-slices
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        qa.v[s] = *reinterpret_cast<const bf16x8*>(&s_q[tb][col][32 * s + 8 * g]);
+        da.v[s] = *reinterpret_cast<const bf16x8*>(&s_do[tb][col][32 * s + 8 * g]);
+      }
+      const floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});    // [head 4 g + r][key col]
+      const floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
+      bf16x4 pb, db;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 st = s_st[tb][4 * g + r];
+        const float p = key > t ? 0.f : exp2f(fmaf(sacc[r], c2, -st.x));
+        pb[r] = (__bf16)p;
+        db[r] = (__bf16)(p * (pacc[r] - st.y));
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const bf16x4 doa = *reinterpret_cast<const bf16x4*>(&s_dot[tb][16 * dt + col][4 * g]);
+        const bf16x4 qta = *reinterpret_cast<const bf16x4*>(&s_qt[tb][16 * dt + col][4 * g]);
+        dv[dt] = mfma_k16(doa, pb, dv[dt]);                // [d 16 dt + 4 g + r][key col]
+        dk[dt] = mfma_k16(qta, db, dk[dt]);
+      }
+    }
+    __syncthreads();
+  }
+  float* pk = a.partial + (int64_t)item * 2 * kLeaf * D;
+  float* pv = pk + kLeaf * D;
+  const int kr = 16 * wave + col;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    *reinterpret_cast<float4*>(pk + kr * D + 16 * dt + 4 * g) = make_float4(dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]);
+    *reinterpret_cast<float4*>(pv + kr * D + 16 * dt + 4 * g) = make_float4(dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
+  }
+}
+
+// dk, dv of every key: the block's item partials added in item order (zero for blocks that
+// no token selected), dk scaled once.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_finish_kernel(BwdArgs a) {
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (e, key row, 4-column group)
+  if (x >= (int64_t)a.batch * a.n_kv_heads * m1 * kLeaf * (D / 4)) return;
+  const int d4 = (int)(x % (D / 4));
+  const int kr = (int)((x / (D / 4)) % kLeaf);
+  const int64_t e = x / ((D / 4) * kLeaf);
+  const int bh = (int)(e / m1), j = (int)(e % m1);
+  const int64_t key = (int64_t)j * kLeaf + kr;
+  if (key >= a.n) return;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int items = (a.seg_len[e] + kBwdItem - 1) / kBwdItem;
+  const int64_t first = a.item_base[e];
+  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+  for (int i = 0; i < items; ++i) {
+    const float* pk = a.partial + (first + i) * 2 * kLeaf * D + kr * D + 4 * d4;
+    const float4 xk = *reinterpret_cast<const float4*>(pk);
+    const float4 xv = *reinterpret_cast<const float4*>(pk + kLeaf * D);
+    sk.x += xk.x; sk.y += xk.y; sk.z += xk.z; sk.w += xk.w;
+    sv.x += xv.x; sv.y += xv.y; sv.z += xv.z; sv.w += xv.w;
+  }
+  float* ok = a.dk + b * a.dk_sb + key * a.dk_st + (int64_t)kvh * a.dk_sh + 4 * d4;
+  float* ov = a.dv + b * a.dv_sb + key * a.dv_st + (int64_t)kvh * a.dv_sh + 4 * d4;
+  *reinterpret_cast<float4*>(ok) = make_float4(sk.x * a.scale, sk.y * a.scale, sk.z * a.scale, sk.w * a.scale);
+  *reinterpret_cast<float4*>(ov) = sv;
+}
+
+// ----------------------------------------------------------------------------- launcher
+template <typename TD, int D>
+hipError_t launch_attention_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int bhs = a.batch * a.n_kv_heads;
+  const int m1 = ceil_div(a.n, kLeaf);
+  const int chunks = ceil_div(a.n, kBwdChunk);
+  const int64_t blocks = (int64_t)bhs * m1;
+  hipError_t e;
+
+  PackArgs p;                                           // K rows
+  p.k = a.k; p.k_sb = a.k_sb; p.k_st = a.k_st; p.k_sh = a.k_sh;
+  p.v = nullptr; p.v_sb = p.v_st = p.v_sh = 0;
+  p.kpack = a.kpack; p.vpack = nullptr;
+  p.batch = a.batch; p.n_kv_heads = a.n_kv_heads; p.head_dim = D; p.n = a.n;
+  if ((e = launch_pack(p, s)) != hipSuccess) return e;
+  p.k = a.v; p.k_sb = a.v_sb; p.k_st = a.v_st; p.k_sh = a.v_sh;      // V rows, K in the value layout
+  p.v = a.k; p.v_sb = a.k_sb; p.v_st = a.k_st; p.v_sh = a.k_sh;
+  p.kpack = a.vrows; p.vpack = a.kcols;
+  if ((e = launch_pack(p, s)) != hipSuccess) return e;
+
+  const dim3 tok_grid(ceil_div(a.n, 4), bhs);
+  hipLaunchKernelGGL((bwd_stats_kernel<TD>), tok_grid, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t rank_lds = (size_t)(kBwdChunk * a.top_k + m1) * sizeof(int32_t);
+  hipLaunchKernelGGL(bwd_rank_kernel, dim3(chunks, bhs), dim3(256), rank_lds, s, a, chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned blk_grid = (unsigned)((blocks + 255) / 256);
+  hipLaunchKernelGGL(bwd_colscan_kernel, dim3(blk_grid), dim3(256), 0, s, a, chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, s, a, blocks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_items_kernel, dim3(blk_grid), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = (int64_t)bhs * a.n;
+  hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<TD, D>), tok_grid, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<TD, D>), dim3((unsigned)a.max_items), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t fin = blocks * kLeaf * (D / 4);
+  hipLaunchKernelGGL((attn_bwd_finish_kernel<D>), dim3((unsigned)((fin + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename TD>
+hipError_t launch_attention_bwd_d(const BwdArgs& a, hipStream_t s) {
+  return a.head_dim == 64 ? launch_attention_bwd_t<TD, 64>(a, s) : launch_attention_bwd_t<TD, 128>(a, s);
+}
+
+hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s) {
+  return a.grad_bf16 ? launch_attention_bwd_d<__bf16>(a, s) : launch_attention_bwd_d<float>(a, s);
+}
+
+}  // namespace pisa

@@ -166,11 +166,16 @@ def _draw_v(w: Workload, b: int, kvh: int, n: int) -> np.ndarray:
     return _rng(w.seed, 2, b, kvh).standard_normal((n, w.head_dim), dtype=np.float32)
 
 
-_DRAW = {"q": _draw_q, "k": _draw_k, "v": _draw_v}
+def _draw_do(w: Workload, b: int, h: int, n: int) -> np.ndarray:
+    return _rng(w.seed, 3, b, h).standard_normal((n, w.head_dim), dtype=np.float32)
+
+
+_DRAW = {"q": _draw_q, "k": _draw_k, "v": _draw_v, "do": _draw_do}
 
 
 def draw(w: Workload, which: str, b: int, h: int, n: int | None = None, bits: bool = False) -> np.ndarray:
-    """One [n, d] slice of Q ('q', head h) or K / V ('k' / 'v', KV head h) of sequence b.
+    """One [n, d] slice of Q ('q', head h), K / V ('k' / 'v', KV head h) or the upstream
+    gradient of the attention output ('do', head h) of sequence b.
 
     Returns float32 values rounded to the workload dtype, or with ``bits`` the
     storage form (float32 for fp32 workloads, uint16 bfloat16 patterns otherwise).
@@ -234,3 +239,48 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     return round_bf16_bits(x)
+
+
+def grad_output(w: Workload, batches=None, n: int | None = None) -> np.ndarray:
+    """Upstream gradient dO [B, n, Hq, d] of the attention output: N(0,1), rounded to the workload dtype
+    (float32 values)."""
+    import concurrent.futures
+
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    n = w.seq_len if n is None else n
+    out = np.empty((len(batches), n, w.n_q_heads, w.head_dim), dtype=np.float32)
+
+    def fill(job):
+        bi, b, h = job
+        out[bi, :, h] = draw(w, "do", b, h, n)
+
+    jobs = [(bi, b, h) for bi, b in enumerate(batches) for h in range(w.n_q_heads)]
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        list(ex.map(fill, jobs))
+    return out
+
+
+def random_selection(w: Workload, K: int, b: int, kvh: int, n: int | None = None) -> np.ndarray:
+    """A valid block selection [n, K] int32 for (b, kvh): row t lists min(K, t // 64 + 1) distinct
+    blocks j <= t // 64, ascending, padded with -1; rows with more candidates than K take K of them
+    uniformly.  Drawn from ``rng([seed, 20, b, kvh])``; used as a fixed input of the attention
+    gradients, independent of any scoring."""
+    n = w.seq_len if n is None else n
+    rng = _rng(w.seed, 20, b, kvh)
+    m = np.arange(n) // w.block + 1                            # candidate blocks of each row
+    out = np.full((n, K), -1, dtype=np.int32)
+    small = m <= K
+    for c in np.unique(m[small]):
+        out[m == c, :c] = np.arange(c, dtype=np.int32)
+    rows = np.nonzero(~small)[0]
+    if rows.size:
+        keys = rng.random((rows.size, 4 * K))
+        cand = np.floor(keys * m[rows, None]).astype(np.int64)
+        for r, row in enumerate(rows):
+            picked = np.unique(cand[r])
+            while picked.size < K:                             # rare: fewer than K distinct draws
+                extra = np.floor(rng.random(4 * K) * m[row]).astype(np.int64)
+                picked = np.unique(np.concatenate([picked, extra]))
+            chosen = rng.permutation(picked)[:K]
+            out[row] = np.sort(chosen)
+    return out

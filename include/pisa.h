@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 3
+#define PISA_ABI_VERSION 4
 
 typedef enum {
   PISA_OK = 0,
@@ -199,6 +199,45 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  */
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by pisa_sparse_attn_bwd for cfg (0 for an unsupported
+ * cfg): packed copies of K and V (3 * B * H_kv * ceil(N / 64) * 64 * d * 2
+ * bytes), per-row statistics, the inverse of the selection lists, and per-item
+ * dk / dv partial sums (about (B * H_kv * N * K / 512 + B * H_kv * ceil(N / 64))
+ * * 64 * d * 8 bytes). */
+size_t pisa_attn_bwd_workspace_bytes(const pisa_cfg* cfg);
+
+/*
+ * sparse_attn_bwd - gradients of sparse_attn_fwd (Prerequisites, block sparse
+ * attention; Method steps, fourth step) with the selected sets held fixed: the
+ * page calls the method trainable but states no gradient, and the selection is
+ * piecewise constant in q and k, so only the softmax attention over the
+ * selected keys is differentiated.  For token t, head h and selected key r:
+ * P = softmax(scale q . k_r), dv_r += P dO, dS = P (dO . v_r - dO . O),
+ * dq = scale sum_r dS k_r, dk_r += scale dS q.
+ *   q, k, v  : bfloat16 (cfg->dtype must be PISA_BF16), as in sparse_attn_fwd
+ *   sel      : int32 [B][H_kv][N][K] as given to sparse_attn_fwd; an entry takes
+ *              part if 0 <= j <= t / 64 and no earlier slot of the row lists
+ *              j (select_blocks rows always satisfy this)
+ *   o, dout  : [B][N][H_q][d] forward output and its upstream gradient, both of
+ *              element type grad_dtype (float32 or bfloat16); dout enters the
+ *              products rounded to bfloat16
+ *   row_lse  : float32 [B][H_q][N], the row LSE written by sparse_attn_fwd
+ *   dq       : float32 [B][N][H_q][d] output (every row written; zero for a
+ *              token with no block in use)
+ *   dk, dv   : float32 [B][N][H_kv][d] outputs (every row written; zero for
+ *              keys no token selects)
+ *   ws       : workspace of >= pisa_attn_bwd_workspace_bytes(cfg) bytes,
+ *              256-byte aligned
+ * Products run on bf16 MFMA with fp32 accumulation; P and dS enter the second
+ * products rounded to bfloat16.  Results are deterministic (no atomics).
+ * Returns PISA_ERR_UNSUPPORTED for fp32 inputs, for ceil(N / 64) > 8192 and
+ * when B * H_kv * N * K exceeds 2^31 - 1.
+ */
+pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, pisa_dtype grad_dtype,
+                                 const float* row_lse, pisa_tensor_mut dq, pisa_tensor_mut dk, pisa_tensor_mut dv,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /*

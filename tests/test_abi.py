@@ -16,10 +16,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_symbols()
-    assert len(declared) == 13
+    assert len(declared) == 15
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 3
+    assert lib.pisa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -108,3 +108,32 @@ def test_flat_selection_validation_and_workspace(lib):
     wide = _cfg(top_k=17)
     assert lib.pisa_select_flat(ctypes.byref(wide), good, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
                                 ctypes.c_void_p(4096), 1 << 30, None) == 2                 # K > 16
+
+
+def test_backward_validation_and_workspace(lib):
+    """The backward takes bf16 inputs, at most 8192 leaves, a float32 or bfloat16 gradient type
+    and its full workspace; everything is checked before any launch."""
+    import torch
+
+    cfg = _cfg(batch=1, seq_len=4096, n_q_heads=16, n_kv_heads=1, top_k=16)
+    ws = lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(cfg))
+    m1, slots = 64, 4096 * 16
+    max_items = slots // 512 + m1
+    assert ws >= 3 * m1 * 64 * 128 * 2 + 4096 * 16 * 8 + 2 * slots * 4 + max_items * 2 * 64 * 128 * 4
+    assert lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(_cfg(dtype=torch.float32))) == 0
+    assert lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(_cfg(seq_len=8192 * 64 + 1))) == 0
+    assert lib.pisa_attn_bwd_workspace_bytes(ctypes.byref(_cfg(seq_len=8192 * 64))) > 0
+    good = binding.PisaTensor(4096, 0, 128, 128)
+    bad = binding.PisaTensor(4100, 0, 128, 128)
+    lse = ctypes.c_void_p(4096)
+
+    def call(c=cfg, gd=0, q=good, dq=good, w=ctypes.c_void_p(4096), wlen=1 << 40, lse_ptr=lse):
+        return lib.pisa_sparse_attn_bwd(ctypes.byref(c), q, good, good, ctypes.c_void_p(4096), good, good, gd,
+                                        lse_ptr, dq, good, good, w, wlen, None)
+
+    assert call(c=_cfg(dtype=torch.float32)) == 2            # fp32 inputs unsupported
+    assert call(wlen=16) == 3                                 # workspace too small
+    assert call(w=ctypes.c_void_p(4096 + 16)) == 3            # workspace not 256-byte aligned
+    assert call(gd=5) == 1                                    # gradient type
+    assert call(q=bad) == 1 and call(dq=bad) == 1             # misaligned tensors
+    assert call(lse_ptr=None) == 1                            # row LSE required
