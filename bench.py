@@ -122,7 +122,7 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     from hierarchical_top_selection_amd import binding
 
     q, k, v = _device_inputs(w)
-    _INPUTS[w.name] = (q, k)
+    _INPUTS[w.name] = (q, k, v)
     B, N, Hq, d = q.shape
     K = w.top_k
     pyr = torch.empty((B, w.n_kv_heads, binding.pyramid_nodes(N), d), dtype=torch.float32, device=q.device)
@@ -232,6 +232,52 @@ def variant_selection(q, k, n_kv_heads: int, K: int, reps: int = 5) -> dict:
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
         out[f"{score}_select_ms"] = sorted(times)[len(times) // 2]
+    return out
+
+
+def run_backward(q, k, v, n_kv_heads: int, K: int, reps: int = 5) -> dict:
+    """Attention gradients of one prefill: selection and forward once (untimed), then the median
+    of `reps` timed calls of sparse_attn_bwd (HIP events on the current stream).
+
+    dO is drawn on the device (seeded torch generator, N(0,1), float32); the forward output is
+    float32.  Work counts valid (head, key) pairs like the forward: the dq pass does 3 products
+    and the dk/dv pass 4, 14 d flops per pair in all.
+    """
+    import torch
+
+    from hierarchical_top_selection_amd import binding
+
+    B, N, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    pyr = binding.build_pyramid(k)
+    sel = binding.select_blocks(q, k, pyr, K)
+    o, lse = binding.sparse_attn_fwd(q, k, v, sel, return_lse=True, out_dtype=torch.float32)
+    gen = torch.Generator(device=q.device)
+    gen.manual_seed(7)
+    dout = torch.randn(o.shape, generator=gen, device=q.device, dtype=torch.float32)
+    cfg = binding.make_cfg(B, N, Hq, n_kv_heads, d, K, q.dtype)
+    ws = torch.empty(binding.attn_bwd_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+
+    def fn():
+        binding.sparse_attn_bwd(q, k, v, sel, o, lse, dout, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    fn()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    flops = attention_flops(sel, N, G, d) * 14.0 / 4.0
+    out = {"K": K, "bwd_ms": ms, "tokens_per_s": B * N / (ms / 1e3), "tflops": flops / (ms * 1e-3) / 1e12,
+           "workspace_gb": ws.numel() / 1e9, "data": "dO: device-drawn N(0,1), seeded torch generator"}
+    del ws, dq, dk, dv, dout, o, lse, sel, pyr
     return out
 
 
@@ -356,6 +402,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing record")
     ap.add_argument("--no-quality", action="store_true", help="skip the selection-quality record")
+    ap.add_argument("--no-backward", action="store_true", help="skip the attention-gradient record")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the hierarchical vs single-level selection sweep (K = 8, N = 4K .. the workload's N)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -389,11 +436,14 @@ def main() -> int:
         extra[name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                        "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"]}
     if not args.no_sweep:
-        q_main, k_main = _INPUTS[w.name]
+        q_main, k_main, _ = _INPUTS[w.name]
         extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
         extra["score_variants"] = variant_selection(q_main, k_main, w.n_kv_heads, w.top_k)
+    if not args.no_backward:
+        q_main, k_main, v_main = _INPUTS[w.name]
+        extra["backward_" + w.name] = run_backward(q_main, k_main, v_main, w.n_kv_heads, w.top_k)
     if not args.no_quality:
-        q_main, k_main = _INPUTS[w.name]
+        q_main, k_main, _ = _INPUTS[w.name]
         extra["selection_quality_k8"] = selection_quality(q_main, k_main, w.n_kv_heads, 8)
         for name in ("quality_diffuse_n65536", "quality_needles_n65536", "quality_runs_n65536"):
             rw = W.WORKLOADS[name]

@@ -125,11 +125,11 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
 }
 
 struct BwdWorkspace {
-  size_t kpack, vrows, kcols, stats, rank, hist, seg_len, seg_base, item_base, list, items, n_items, partial, total;
+  size_t kpack, vrows, kcols, tok, rank, hist, seg_len, seg_base, item_base, list, items, n_items, partial, total;
   int64_t max_items;
 };
 
-// Backward workspace: three packed copies of K / V, the row statistics, the inverse index of
+// Backward workspace: three packed copies of K / V, the token records, the inverse index of
 // the selections and the per-item dK / dV partial sums (see BwdArgs).
 BwdWorkspace bwd_layout(const pisa_cfg* c) {
   BwdWorkspace w;
@@ -142,8 +142,8 @@ BwdWorkspace bwd_layout(const pisa_cfg* c) {
   w.kpack = 0;
   w.vrows = align256(w.kpack + pack);
   w.kcols = align256(w.vrows + pack);
-  w.stats = align256(w.kcols + pack);
-  w.rank = align256(w.stats + (size_t)bh * c->seq_len * 16 * 8);
+  w.tok = align256(w.kcols + pack);
+  w.rank = align256(w.tok + (size_t)bh * c->seq_len * pisa::bwd_record_bytes(c->head_dim));
   w.hist = align256(w.rank + (size_t)slots * 4);
   w.seg_len = align256(w.hist + (size_t)bh * chunks * m1 * 4);
   w.seg_base = align256(w.seg_len + (size_t)bh * m1 * 4);
@@ -393,7 +393,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
   a.vrows = reinterpret_cast<pisa::bf16x8*>(base + w.vrows);
   a.kcols = reinterpret_cast<pisa::bf16x8*>(base + w.kcols);
-  a.stats = reinterpret_cast<float2*>(base + w.stats);
+  a.tok = base + w.tok;
   a.rank = reinterpret_cast<int32_t*>(base + w.rank);
   a.hist = reinterpret_cast<int32_t*>(base + w.hist);
   a.seg_len = reinterpret_cast<int32_t*>(base + w.seg_len);

@@ -17,8 +17,9 @@
 // * dk and dv, key-major: a deterministic inverse of the selection lists each block's
 //   tokens in ascending order (a stable counting sort: per-chunk occurrence ranks, a
 //   per-block scan over chunks, one scan over blocks, a scatter).  A work item is up to
-//   512 tokens of one block; its four waves own 16 keys each, stage the tokens' queries
-//   and output gradients in LDS (row-major and transposed), form S = Q K^T and dP = dO V^T
+//   512 tokens of one block; its four waves own 16 keys each, copy the tokens' records
+//   (bf16 query and output-gradient rows and row statistics, written once per token by a
+//   packing pass) into LDS, double-buffered, form S = Q K^T and dP = dO V^T
 //   with the heads as rows, and accumulate dv^T += dO^T P and dk^T += Q^T dS on the
 //   16x16x16 MFMA, whose contraction runs over the 16 head rows.  Items write partial
 //   sums; a last pass adds each block's partials in item order.  No atomics anywhere, so
@@ -58,39 +59,51 @@ __device__ inline bool slot_in_use(int j, int lane, int K, int t) {
 
 }  // namespace
 
-// ----------------------------------------------------------------------------- row statistics
-// stats[bh][t][h] = (row LSE * log2 e, Delta = dO . O) for the group's heads; +inf / 0 for
-// the padding columns h >= G, which makes their probabilities exactly zero.
-template <typename TD>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.n) return;
+// ----------------------------------------------------------------------------- token records
+// One record per (b, kvh, token) (see BwdArgs): the group's query rows and upstream-gradient
+// rows in bf16 (dO rounded to nearest-even), and per head (row LSE * log2 e, Delta = dO . O)
+// with Delta taken from the unrounded dO; +inf / 0 for the padding heads h >= G, which makes
+// their probabilities exactly zero.  One thread per 16-byte piece; a row's pieces are
+// adjacent lanes, which reduce Delta among themselves.
+template <typename TD, int D>
+__global__ __launch_bounds__(256) void bwd_tokens_kernel(BwdArgs a) {
+  constexpr int kPieces = D / 8;                     // 16-byte pieces per row
+  constexpr int64_t kRec = bwd_record_bytes(D);
+  const int t = blockIdx.x;                          // one token per workgroup of 16 * D / 8 threads
+  const int h = threadIdx.x / kPieces, p = threadIdx.x % kPieces;
   const int bh = blockIdx.y, b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const int g = lane >> 4, col = lane & 15;
-  const int quarter = a.head_dim / 4;
-  float acc = 0.f;
-  if (col < a.group) {
-    const int head = kvh * a.group + col;
-    const TD* orow = reinterpret_cast<const TD*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh +
-                     g * quarter;
-    const TD* drow = reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
-                     (int64_t)head * a.do_sh + g * quarter;
-    for (int i = 0; i < quarter; i += 4) {
-      const float4 x = load4(orow + i), y = load4(drow + i);
-      acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-    }
+  bf16x8 qv, dv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { qv[e] = (__bf16)0.f; dv[e] = (__bf16)0.f; }
+  float dot = 0.f;
+  if (t < a.n && h < a.group) {
+    const int head = kvh * a.group + h;
+    qv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb +
+                                          (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * p);
+    const TD* dp = reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
+                   (int64_t)head * a.do_sh + 8 * p;
+    const TD* op = reinterpret_cast<const TD*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh +
+                   8 * p;
+    const float4 d0 = load4(dp), d1 = load4(dp + 4), o0 = load4(op), o1 = load4(op + 4);
+    dot = d0.x * o0.x + d0.y * o0.y + d0.z * o0.z + d0.w * o0.w + d1.x * o1.x + d1.y * o1.y + d1.z * o1.z +
+          d1.w * o1.w;
+    dv[0] = (__bf16)d0.x; dv[1] = (__bf16)d0.y; dv[2] = (__bf16)d0.z; dv[3] = (__bf16)d0.w;
+    dv[4] = (__bf16)d1.x; dv[5] = (__bf16)d1.y; dv[6] = (__bf16)d1.z; dv[7] = (__bf16)d1.w;
   }
-  acc = wave_add_xor(acc, 16);
-  acc = wave_add_xor(acc, 32);
-  if (g == 0) {
-    float2 st = make_float2(__builtin_huge_valf(), 0.f);
-    if (col < a.group) {
-      const int hq = a.n_kv_heads * a.group;
-      st.x = a.row_lse[((int64_t)b * hq + kvh * a.group + col) * a.n + t] * kLog2e;
-      st.y = acc;
+#pragma unroll
+  for (int m = 1; m < kPieces; m <<= 1) dot += __shfl_xor(dot, m, 64);     // the row's kPieces lanes
+  if (t < a.n) {
+    char* rec = a.tok + ((int64_t)bh * a.n + t) * kRec;
+    *reinterpret_cast<bf16x8*>(rec + (h * D + 8 * p) * 2) = qv;
+    *reinterpret_cast<bf16x8*>(rec + bwd_row_bytes(D) + (h * D + 8 * p) * 2) = dv;
+    if (p == 0) {
+      float2 st = make_float2(__builtin_huge_valf(), 0.f);
+      if (h < a.group) {
+        const int hq = a.n_kv_heads * a.group;
+        st = make_float2(a.row_lse[((int64_t)b * hq + kvh * a.group + h) * a.n + t] * kLog2e, dot);
+      }
+      *reinterpret_cast<float2*>(rec + bwd_stats_offset(D) + 8 * h) = st;
     }
-    a.stats[((int64_t)bh * a.n + t) * 16 + col] = st;
   }
 }
 
@@ -231,7 +244,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     qf.zero();
     df.zero();
   }
-  const float2 st = a.stats[((int64_t)bh * a.n + t) * 16 + col];
+  const float2 st = *reinterpret_cast<const float2*>(a.tok + ((int64_t)bh * a.n + t) * bwd_record_bytes(D) +
+                                                     bwd_stats_offset(D) + 8 * col);
   const float c2 = a.scale * kLog2e;
 
   const int64_t blk = (int64_t)bh * m1 * (kLeaf * D / 8);
@@ -290,16 +304,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------- dk, dv (key-major)
-template <typename TD, int D>
+template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
-  constexpr int kTok = 4;                 // tokens staged per round
-  constexpr int kRow = D + 8;             // padded row of the row-major copies
-  __shared__ __align__(16) __bf16 s_q[kTok][16][kRow];
-  __shared__ __align__(16) __bf16 s_do[kTok][16][kRow];
-  __shared__ __align__(16) __bf16 s_qt[kTok][D][16];
-  __shared__ __align__(16) __bf16 s_dot[kTok][D][16];
-  __shared__ float2 s_st[kTok][16];
-  __shared__ int s_tok[kTok];
+  constexpr int kTok = 4;                               // tokens per round
+  constexpr int kRow = D + 8;                           // padded LDS row (bf16 elements)
+  constexpr int kRec = bwd_record_bytes(D);
+  constexpr int kPieces = kRec / 16;                    // 16-byte pieces per record
+  constexpr int kPer = (kTok * kPieces + 255) / 256;    // pieces per thread per round
+  constexpr int kRowPieces = D / 8;
+  struct Tok {
+    __bf16 q[16][kRow];
+    __bf16 dout[16][kRow];
+    float2 st[16];
+  };
+  __shared__ __align__(16) Tok s_tok[2][kTok];
+  __shared__ int s_list[kBwdItem];                      // the item's tokens
 
   const int item = blockIdx.x;
   if (item >= a.n_items[0]) return;       // uniform over the workgroup
@@ -313,6 +332,38 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int key = j * kLeaf + 16 * wave + col;          // this lane's key column
+  const char* records = a.tok + (int64_t)bh * a.n * kRec;
+  for (int i = threadIdx.x; i < len; i += blockDim.x) s_list[i] = toks[i];
+  __syncthreads();
+
+  // Round r stages tokens [kTok r, kTok r + kTok) of the item: piece c of a record goes to row
+  // c / (D / 8) of q (c < 16 D / 8), of dO, or to the statistics.
+  uint4 stage[kPer];
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = threadIdx.x + 256 * i;
+      const int tb = x / kPieces, c = x % kPieces;
+      if (x < kTok * kPieces && base + tb < len)
+        stage[i] = reinterpret_cast<const uint4*>(records + (int64_t)s_list[base + tb] * kRec)[c];
+    }
+  };
+  auto store = [&](int buf, int base) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = threadIdx.x + 256 * i;
+      const int tb = x / kPieces, c = x % kPieces;
+      if (x < kTok * kPieces && base + tb < len) {
+        Tok& tk = s_tok[buf][tb];
+        uint4* dst;
+        if (c < 16 * kRowPieces) dst = reinterpret_cast<uint4*>(&tk.q[c / kRowPieces][8 * (c % kRowPieces)]);
+        else if (c < 32 * kRowPieces)
+          dst = reinterpret_cast<uint4*>(&tk.dout[(c - 16 * kRowPieces) / kRowPieces][8 * (c % kRowPieces)]);
+        else dst = reinterpret_cast<uint4*>(&tk.st[2 * (c - 32 * kRowPieces)]);
+        *dst = stage[i];
+      }
+    }
+  };
 
   FragBF16<D> kb, vb;                                   // B fragments: key col, d k-slices
   if (key < a.n) {
@@ -330,68 +381,45 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
   }
   const float c2 = a.scale * kLog2e;
 
-  for (int base = 0; base < len; base += kTok) {
+  fetch(0);
+  store(0, 0);
+  __syncthreads();
+  for (int base = 0, buf = 0; base < len; base += kTok, buf ^= 1) {
+    const bool more = base + kTok < len;
+    if (more) fetch(base + kTok);                       // next round's records in flight
     const int nt = min(kTok, len - base);
-    for (int x = threadIdx.x; x < kTok * 16 * (D / 8); x += blockDim.x) {
-      const int tb = x / (16 * (D / 8)), rem = x % (16 * (D / 8));
-      const int h = rem / (D / 8), p = rem % (D / 8);
-      bf16x8 qv, dv8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { qv[i] = (__bf16)0.f; dv8[i] = (__bf16)0.f; }
-      if (tb < nt && h < a.group) {
-        const int t = toks[base + tb];
-        const int hd = kvh * a.group + h;
-        qv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb +
-                                              (int64_t)t * a.q_st + (int64_t)hd * a.q_sh + 8 * p);
-        dv8 = load8_bf16(reinterpret_cast<const TD*>(a.dout) + b * a.do_sb + (int64_t)t * a.do_st +
-                         (int64_t)hd * a.do_sh + 8 * p);
-      }
-      *reinterpret_cast<bf16x8*>(&s_q[tb][h][8 * p]) = qv;
-      *reinterpret_cast<bf16x8*>(&s_do[tb][h][8 * p]) = dv8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s_qt[tb][8 * p + i][h] = qv[i];
-        s_dot[tb][8 * p + i][h] = dv8[i];
-      }
-    }
-    if (threadIdx.x < kTok * 16) {
-      const int tb = threadIdx.x / 16, h = threadIdx.x % 16;
-      float2 st = make_float2(__builtin_huge_valf(), 0.f);
-      int t = -1;
-      if (tb < nt) {
-        t = toks[base + tb];
-        st = a.stats[((int64_t)bh * a.n + t) * 16 + h];
-      }
-      s_st[tb][h] = st;
-      if (h == 0) s_tok[tb] = t;
-    }
-    __syncthreads();
     for (int tb = 0; tb < nt; ++tb) {
-      const int t = s_tok[tb];
+      const Tok& tk = s_tok[buf][tb];
+      const int t = s_list[base + tb];
       FragBF16<D> qa, da;                               // A fragments: head col, d k-slices
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        qa.v[s] = *reinterpret_cast<const bf16x8*>(&s_q[tb][col][32 * s + 8 * g]);
-        da.v[s] = *reinterpret_cast<const bf16x8*>(&s_do[tb][col][32 * s + 8 * g]);
+        qa.v[s] = *reinterpret_cast<const bf16x8*>(&tk.q[col][32 * s + 8 * g]);
+        da.v[s] = *reinterpret_cast<const bf16x8*>(&tk.dout[col][32 * s + 8 * g]);
       }
       const floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});    // [head 4 g + r][key col]
       const floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
       bf16x4 pb, db;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float2 st = s_st[tb][4 * g + r];
-        const float p = key > t ? 0.f : exp2f(fmaf(sacc[r], c2, -st.x));
+        const float2 sr = tk.st[4 * g + r];
+        const float p = key > t ? 0.f : exp2f(fmaf(sacc[r], c2, -sr.x));
         pb[r] = (__bf16)p;
-        db[r] = (__bf16)(p * (pacc[r] - st.y));
+        db[r] = (__bf16)(p * (pacc[r] - sr.y));
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const bf16x4 doa = *reinterpret_cast<const bf16x4*>(&s_dot[tb][16 * dt + col][4 * g]);
-        const bf16x4 qta = *reinterpret_cast<const bf16x4*>(&s_qt[tb][16 * dt + col][4 * g]);
+        bf16x4 doa, qta;                                // A fragments: d row 16 dt + col, heads 4 g + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          doa[r] = tk.dout[4 * g + r][16 * dt + col];
+          qta[r] = tk.q[4 * g + r][16 * dt + col];
+        }
         dv[dt] = mfma_k16(doa, pb, dv[dt]);                // [d 16 dt + 4 g + r][key col]
         dk[dt] = mfma_k16(qta, db, dk[dt]);
       }
     }
+    if (more) store(buf ^ 1, base + kTok);              // that buffer was last read a round ago
     __syncthreads();
   }
   float* pk = a.partial + (int64_t)item * 2 * kLeaf * D;
@@ -455,7 +483,8 @@ hipError_t launch_attention_bwd_t(const BwdArgs& a, hipStream_t s) {
   if ((e = launch_pack(p, s)) != hipSuccess) return e;
 
   const dim3 tok_grid(ceil_div(a.n, 4), bhs);
-  hipLaunchKernelGGL((bwd_stats_kernel<TD>), tok_grid, dim3(256), 0, s, a);
+  const int rec_threads = 16 * (D / 8);                     // one token's pieces
+  hipLaunchKernelGGL((bwd_tokens_kernel<TD, D>), dim3((unsigned)a.n, bhs), dim3(rec_threads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rank_lds = (size_t)(kBwdChunk * a.top_k + m1) * sizeof(int32_t);
   hipLaunchKernelGGL(bwd_rank_kernel, dim3(chunks, bhs), dim3(256), rank_lds, s, a, chunks);
@@ -473,7 +502,7 @@ hipError_t launch_attention_bwd_t(const BwdArgs& a, hipStream_t s) {
 
   hipLaunchKernelGGL((attn_bwd_dq_kernel<TD, D>), tok_grid, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<TD, D>), dim3((unsigned)a.max_items), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D>), dim3((unsigned)a.max_items), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t fin = blocks * kLeaf * (D / 4);
   hipLaunchKernelGGL((attn_bwd_finish_kernel<D>), dim3((unsigned)((fin + 255) / 256)), dim3(256), 0, s, a);

@@ -97,7 +97,10 @@ struct AttnArgs {
 };
 
 // Gradients of the block-sparse attention with the selections held fixed (bf16 q, k, v).
-//   stats   [B*Hkv][N][16] float2: (row LSE * log2 e, Delta = dO . O) per head, +inf / 0 past G
+//   tok     [B*Hkv][N] token records of bwd_record_bytes(d) bytes: the group's queries and
+//           upstream gradients as bf16 rows [16][d] (heads past G zero) and per head
+//           (row LSE * log2 e, Delta = dO . O) as float2 [16] (+inf / 0 past G): everything
+//           the key-major pass stages for a token, one contiguous copy
 //   rank    [B*Hkv][N][K] int32: occurrence of (t, slot)'s block among earlier tokens of its chunk
 //   hist    [B*Hkv][chunks][M1] int32: per-chunk block counts, then their exclusive prefix per block
 //   seg_len, seg_base, item_base [B*Hkv*M1] int32: tokens selecting each block, their list offset,
@@ -128,7 +131,7 @@ struct BwdArgs {
   bf16x8* kpack;         // K rows (attention K layout)
   bf16x8* vrows;         // V rows in the K layout
   bf16x8* kcols;         // K in the V^T layout
-  float2* stats;
+  char* tok;
   int32_t* rank;
   int32_t* hist;
   int32_t* seg_len;
@@ -143,6 +146,11 @@ struct BwdArgs {
   float scale;
   bool grad_bf16;        // element type of o and dout
 };
+
+// Token record geometry (bytes): rows of q, rows of dO, the statistics.
+__host__ __device__ constexpr int bwd_row_bytes(int d) { return 16 * d * 2; }
+__host__ __device__ constexpr int bwd_stats_offset(int d) { return 2 * bwd_row_bytes(d); }
+__host__ __device__ constexpr int bwd_record_bytes(int d) { return bwd_stats_offset(d) + 16 * 8; }
 
 constexpr int kBwdChunk = 256;      // tokens per ranking chunk
 constexpr int kBwdItem = 512;       // tokens per key-major work item
