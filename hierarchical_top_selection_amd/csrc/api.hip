@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "attention_bwd.h"
 #include "kernels.h"
 #include "pisa.h"
 

@@ -24,7 +24,7 @@
 //   16x16x16 MFMA, whose contraction runs over the 16 head rows.  Items write partial
 //   sums; a last pass adds each block's partials in item order.  No atomics anywhere, so
 //   repeated calls give identical bits.
-#include "kernels.h"
+#include "attention_bwd.h"
 
 namespace pisa {
 
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool masked = edge && 32 * (mt >> 1) + 4 * (mt & 1) + r > lim;
-        const float p = masked ? 0.f : exp2f(fmaf(s_acc[mt][r], c2, -st.x));
+        const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s_acc[mt][r], c2, -st.x));
         db[mt >> 1][4 * (mt & 1) + r] = (__bf16)(p * (p_acc[mt][r] - st.y));
       }
 #pragma unroll
@@ -388,24 +388,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
     const bool more = base + kTok < len;
     if (more) fetch(base + kTok);                       // next round's records in flight
     const int nt = min(kTok, len - base);
-    for (int tb = 0; tb < nt; ++tb) {
-      const Tok& tk = s_tok[buf][tb];
-      const int t = s_list[base + tb];
-      FragBF16<D> qa, da;                               // A fragments: head col, d k-slices
+    // S and dP of the round's first token, then per token: P and dS, the next token's S and dP
+    // (independent work the scheduler can overlap), this token's dv and dk products.
+    FragBF16<D> qa, da;                                 // A fragments: head col, d k-slices
+    auto load_rows = [&](const Tok& tk) {
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         qa.v[s] = *reinterpret_cast<const bf16x8*>(&tk.q[col][32 * s + 8 * g]);
         da.v[s] = *reinterpret_cast<const bf16x8*>(&tk.dout[col][32 * s + 8 * g]);
       }
-      const floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});    // [head 4 g + r][key col]
-      const floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
+    };
+    load_rows(s_tok[buf][0]);
+    floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});           // [head 4 g + r][key col]
+    floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
+    for (int tb = 0; tb < nt; ++tb) {
+      const Tok& tk = s_tok[buf][tb];
+      const int t = s_list[base + tb];
       bf16x4 pb, db;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float2 sr = tk.st[4 * g + r];
-        const float p = key > t ? 0.f : exp2f(fmaf(sacc[r], c2, -sr.x));
+        const float p = key > t ? 0.f : __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, -sr.x));
         pb[r] = (__bf16)p;
         db[r] = (__bf16)(p * (pacc[r] - sr.y));
+      }
+      if (tb + 1 < nt) {
+        load_rows(s_tok[buf][tb + 1]);
+        sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});
+        pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
