@@ -197,13 +197,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         const float s1 = __shfl(pscore[1], src, 64);
         if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
       }
-      // exact rank among the candidates; lane j's values are read into scalar registers
-      int rank = 0;
-      for (int j = 0; j < span; ++j) {
-        const float uj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), j));
-        const int cj = __builtin_amdgcn_readlane(cand, j);
-        rank += (int)((cj >= 0) & ((uj > u) | ((uj == u) & (cj < cand))));
+      // exact rank among the candidates by (score descending, index ascending), as one 64-bit key:
+      // the score's bits made order-preserving above the complemented index; empty lanes are 0,
+      // below every candidate.  Lane j's key is read into scalar registers.
+      const uint32_t ubits = __builtin_bit_cast(uint32_t, u + 0.f);          // -0 compares as +0
+      const uint32_t khi = cand >= 0 ? ((ubits & 0x80000000u) ? ~ubits : (ubits | 0x80000000u)) : 0u;
+      const uint32_t klo = cand >= 0 ? 0xffffffffu - (uint32_t)cand : 0u;
+      const uint64_t key = ((uint64_t)khi << 32) | klo;
+      // lanes past `span` hold key 0 and never count, so the loop runs to a multiple of 4
+      auto key_of = [&](int j) {
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(khi, j) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(klo, j);
+      };
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      for (int j = 0; j < span; j += 4) {
+        r0 += (int)(key_of(j) > key);
+        r1 += (int)(key_of(j + 1) > key);
+        r2 += (int)(key_of(j + 2) > key);
+        r3 += (int)(key_of(j + 3) > key);
       }
+      const int rank = r0 + r1 + r2 + r3;
       keep = cand >= 0 && rank < a.top_k;
     }
     // expand the survivors into their causally valid children
