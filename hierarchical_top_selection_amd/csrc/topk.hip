@@ -23,20 +23,27 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int n_valid = __popcll(__ballot(c >= 0));
   bool keep = c >= 0;
   if (n_valid > a.top_k) {
+    // rank by (score descending, leaf ascending) as one 64-bit key: the score's bits made
+    // order-preserving above the complemented leaf index; empty slots are 0, below every
+    // candidate.  Lane j's key is read into scalar registers.
+    const uint32_t ubits = __builtin_bit_cast(uint32_t, u + 0.f);          // -0 compares as +0
+    const uint32_t khi = c >= 0 ? ((ubits & 0x80000000u) ? ~ubits : (ubits | 0x80000000u)) : 0u;
+    const uint32_t klo = c >= 0 ? 0xffffffffu - (uint32_t)c : 0u;
+    const uint64_t key = ((uint64_t)khi << 32) | klo;
     int rank = 0;
     for (int j = 0; j < a.width; ++j) {
-      const float uj = __shfl(u, j, 64);
-      const int cj = __shfl(c, j, 64);
-      rank += (cj >= 0) && (uj > u || (uj == u && cj < c));
+      const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(khi, j) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(klo, j);
+      rank += (int)(kj > key);
     }
     keep = keep && rank < a.top_k;
   }
   const uint64_t kept = __ballot(keep);
   const int m = __popcll(kept);
-  int pos = 0;
+  int pos = 0;                                          // kept candidates with a lower leaf index
   for (int j = 0; j < a.width; ++j) {
-    const int cj = __shfl(c, j, 64);
-    pos += (int)((kept >> j) & 1ull) & (cj < c);
+    const int cj = __builtin_amdgcn_readlane(c, j);
+    pos += (int)(((kept >> j) & 1ull) != 0 && cj < c);
   }
   int32_t* sel = a.sel + row * a.top_k;
   float* sel_u = a.sel_u ? a.sel_u + row * a.top_k : nullptr;
