@@ -247,6 +247,9 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.lv = make_levels(N, N);
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
   r.pairs = split_pairs(r.lv, r.pair_off);
+  pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
+  pisa::bf16x8* qpack = reinterpret_cast<pisa::bf16x8*>(base + w.qpack);
+  r.qpack = bf16 ? qpack : nullptr;                   // routing writes the packed query groups
   if (bf16 && (st = hip_status(pisa::launch_split_summaries(r, s))) != PISA_OK) return st;
   if ((st = hip_status(pisa::launch_route(r, s))) != PISA_OK) return st;
 
@@ -257,8 +260,6 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   c.items = items; c.n_items = n_items; c.item_cap = w.item_cap;
   if ((st = hip_status(pisa::launch_cluster(c, s))) != PISA_OK) return st;
 
-  pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
-  pisa::bf16x8* qpack = reinterpret_cast<pisa::bf16x8*>(base + w.qpack);
   if (bf16) {
     pisa::PackArgs p;
     p.k = k.ptr; p.k_sb = k.stride_b; p.k_st = k.stride_t; p.k_sh = k.stride_h;
@@ -266,11 +267,6 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
     p.kpack = kpack; p.vpack = nullptr;
     p.batch = cfg->batch; p.n_kv_heads = cfg->n_kv_heads; p.head_dim = cfg->head_dim; p.n = N;
     if ((st = hip_status(pisa::launch_pack(p, s))) != PISA_OK) return st;
-    pisa::QPackArgs qp;
-    qp.q = q.ptr; qp.q_sb = q.stride_b; qp.q_st = q.stride_t; qp.q_sh = q.stride_h;
-    qp.qpack = qpack;
-    qp.batch = cfg->batch; qp.n_kv_heads = cfg->n_kv_heads; qp.group = G; qp.head_dim = cfg->head_dim; qp.n = N;
-    if ((st = hip_status(pisa::launch_pack_queries(qp, s))) != PISA_OK) return st;
   }
 
   pisa::LeafArgs l;

@@ -31,6 +31,12 @@ struct RouteArgs {
   int64_t pair_off[kMaxLevels];
   int64_t pairs;
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
+  // bf16 inputs: packed query groups, written on the way (or null).  The G heads of (b, kvh) at
+  // token t occupy G d / 8 sixteen-byte pieces at ((b * Hkv + kvh) * N + t) * G d / 8; piece
+  // (s, g, col), s < d / 32, g < 4, col < G, at (4 s + g) * G + col holds elements
+  // [32 s + 8 g, +8) of head kvh * G + col, so the MFMA B fragment of a query (lane 16 g + col)
+  // is one contiguous run.
+  bf16x8* qpack;
   int batch, n_kv_heads, group, head_dim, n, top_k;
   int score;          // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
@@ -62,7 +68,7 @@ struct LeafArgs {
   const int32_t* n_items;
   float* leaf_u;         // [B*Hkv][N][2K]
   const bf16x8* kpack;   // bf16 inputs: packed K blocks (PackArgs layout)
-  const bf16x8* qpack;   // bf16 inputs: packed query groups (QPackArgs layout)
+  const bf16x8* qpack;   // bf16 inputs: packed query groups (RouteArgs::qpack layout)
   int batch, n_kv_heads, group, head_dim, n, width, n_leaves, window, n_windows, item_cap;
   int score;             // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
@@ -115,16 +121,6 @@ struct PackArgs {
   int batch, n_kv_heads, head_dim, n;
 };
 
-// Packed bf16 query groups: the G heads of (b, kvh) at token t occupy G d / 8 sixteen-byte
-// pieces at ((b * Hkv + kvh) * N + t) * G d / 8; piece (s, g, col), s < d / 32, g < 4, col < G,
-// at (4 s + g) * G + col holds elements [32 s + 8 g, +8) of head kvh * G + col, so the MFMA
-// B fragment of a query (lane 16 g + col) is one contiguous run.
-struct QPackArgs {
-  const void* q;
-  int64_t q_sb, q_st, q_sh;
-  bf16x8* qpack;
-  int batch, n_kv_heads, group, head_dim, n;
-};
 
 // Key order inside a packed K block: M-tile mt = 2 kb + h, row m holds key
 // 32 kb + 8 (m / 4) + 4 h + m % 4.  In an S^T = K Q^T result lane group g of tiles (2 kb, 2 kb + 1)
@@ -172,7 +168,6 @@ struct DecodeArgs {
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
-hipError_t launch_pack_queries(const QPackArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // bf16 inputs: fills a.split from a.pyr.
 hipError_t launch_split_summaries(const RouteArgs& a, hipStream_t s);

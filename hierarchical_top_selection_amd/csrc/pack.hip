@@ -53,32 +53,6 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(PackArgs a) {
   }
 }
 
-// One thread per 16-byte piece of the packed query groups.
-template <int D>
-__global__ __launch_bounds__(256) void pack_queries_kernel(QPackArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_token = a.group * D / 8;
-  const int64_t row = e / per_token;                       // (b * Hkv + kvh) * N + t
-  if (row >= (int64_t)a.batch * a.n_kv_heads * a.n) return;
-  const int p = (int)(e % per_token);
-  const int col = p % a.group, sg = p / a.group;           // sg = 4 s + g
-  const int t = (int)(row % a.n), bh = (int)(row / a.n);
-  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const __bf16* src = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st +
-                      (int64_t)(kvh * a.group + col) * a.q_sh + 8 * sg;   // 32 s + 8 g = 8 (4 s + g)
-  a.qpack[e] = *reinterpret_cast<const bf16x8*>(src);
-}
-
-hipError_t launch_pack_queries(const QPackArgs& a, hipStream_t s) {
-  const int64_t pieces = (int64_t)a.batch * a.n_kv_heads * a.n * a.group * a.head_dim / 8;
-  const unsigned blocks = (unsigned)((pieces + 255) / 256);
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL(pack_queries_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(pack_queries_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   const dim3 grid(ceil_div(a.n, kLeaf), a.batch * a.n_kv_heads);
   if (a.head_dim == 64)

@@ -10,7 +10,8 @@
 // i owns candidate i, a level keeps K of them by exact rank (score descending,
 // node index ascending) and the survivors expand into the next list with a
 // ballot/bit-select compaction.  The leaf candidates (at most 2K per token) are
-// the only output.
+// the output, and for bf16 inputs the query rows it loads are also stored in the
+// leaf stage's packed query layout.
 //
 // Scores need close to single precision (near-ties between candidates are
 // common).  fp32 queries use fp32 summaries on v_mfma_f32_16x16x4_f32.  bf16
@@ -145,6 +146,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
     const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st +
                     (int64_t)(kvh * a.group + col) * a.q_sh;
     Ops::load_q(qf, qrow, g);
+    if constexpr (sizeof(T) == 2) {
+      if (a.qpack) {                                   // the leaf stage's packed copy of this query group
+        bf16x8* dst = a.qpack + ((int64_t)bh * a.n + t) * (a.group * D / 8) + g * a.group + col;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) dst[4 * s * a.group] = qf.h.v[s];
+      }
+    }
   } else {
     Ops::zero_q(qf);
   }
