@@ -16,7 +16,9 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kMaxSeqSelect = 1000000;     // leaf counters of one window must fit in LDS
 constexpr int kMaxSeq = (1 << 25) - 1;     // packed (token << 6 | slot) fits int32
-constexpr int kWindow = 1024;              // tokens per Stage-2 clustering window
+// Tokens per Stage-2 clustering window: a window's query rows and the key blocks its
+// items stream share the L2; measured best at 512 tokens up to 64K and 1024 above.
+int window_tokens(int seq_len) { return seq_len <= 65536 ? 512 : 1024; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -101,13 +103,14 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   const int64_t bh = (int64_t)c->batch * c->n_kv_heads;
   const int64_t slots = bh * c->seq_len * 2 * c->top_k;
   const int m1 = (c->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
-  w.n_windows = (c->seq_len + kWindow - 1) / kWindow;
+  const int window = window_tokens(c->seq_len);
+  w.n_windows = (c->seq_len + window - 1) / window;
   w.cand = 0;
   w.leaf_u = align256(w.cand + slots * 4);
   w.pairs = align256(w.leaf_u + slots * 4);
   w.leaf_off = align256(w.pairs + slots * 4);
   // items per window: sum over leaves of ceil(count / P) <= window pairs / P + distinct leaves
-  const int64_t window_pairs = (int64_t)kWindow * 2 * c->top_k;
+  const int64_t window_pairs = (int64_t)window * 2 * c->top_k;
   w.item_cap = (int)((window_pairs + pisa::kPairsPerItem - 1) / pisa::kPairsPerItem +
                      (m1 < window_pairs ? m1 : window_pairs));
   w.items = align256(w.leaf_off + (size_t)bh * w.n_windows * (m1 + 1) * 4);
@@ -256,7 +259,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   pisa::ClusterArgs c;
   c.cand = cand; c.pairs = pairs; c.leaf_off = leaf_off;
   c.batch = cfg->batch; c.n_kv_heads = cfg->n_kv_heads; c.n = N; c.width = width;
-  c.n_leaves = m1; c.window = kWindow; c.n_windows = w.n_windows;
+  c.n_leaves = m1; c.window = window_tokens(N); c.n_windows = w.n_windows;
   c.items = items; c.n_items = n_items; c.item_cap = w.item_cap;
   if ((st = hip_status(pisa::launch_cluster(c, s))) != PISA_OK) return st;
 
@@ -274,7 +277,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   l.k = k.ptr; l.k_sb = k.stride_b; l.k_st = k.stride_t; l.k_sh = k.stride_h;
   l.pairs = pairs; l.leaf_off = leaf_off; l.leaf_u = leaf_u;
   l.batch = cfg->batch; l.n_kv_heads = cfg->n_kv_heads; l.group = G; l.head_dim = cfg->head_dim;
-  l.n = N; l.width = width; l.n_leaves = m1; l.window = kWindow; l.n_windows = w.n_windows;
+  l.n = N; l.width = width; l.n_leaves = m1; l.window = window_tokens(N); l.n_windows = w.n_windows;
   l.items = items; l.n_items = n_items; l.item_cap = w.item_cap;
   l.scale = scale; l.bf16 = bf16; l.score = cfg->score;
   l.kpack = kpack; l.qpack = qpack;
