@@ -129,11 +129,11 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
 }
 
 struct BwdWorkspace {
-  size_t kpack, vrows, kcols, tok, rank, hist, seg_len, seg_base, item_base, list, items, n_items, partial, total;
+  size_t kpack, vrows, tok, rank, hist, seg_len, seg_base, item_base, list, items, n_items, partial, total;
   int64_t max_items;
 };
 
-// Backward workspace: three packed copies of K / V, the token records, the inverse index of
+// Backward workspace: packed K rows and V rows, the token records, the inverse index of
 // the selections and the per-item dK / dV partial sums (see BwdArgs).
 BwdWorkspace bwd_layout(const pisa_cfg* c) {
   BwdWorkspace w;
@@ -145,8 +145,7 @@ BwdWorkspace bwd_layout(const pisa_cfg* c) {
   w.max_items = slots / pisa::kBwdItem + bh * m1;         // sum over blocks of ceil(len / 512)
   w.kpack = 0;
   w.vrows = align256(w.kpack + pack);
-  w.kcols = align256(w.vrows + pack);
-  w.tok = align256(w.kcols + pack);
+  w.tok = align256(w.vrows + pack);
   w.rank = align256(w.tok + (size_t)bh * c->seq_len * pisa::bwd_record_bytes(c->head_dim));
   w.hist = align256(w.rank + (size_t)slots * 4);
   w.seg_len = align256(w.hist + (size_t)bh * chunks * m1 * 4);
@@ -392,7 +391,6 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.dv = static_cast<float*>(dv.ptr); a.dv_sb = dv.stride_b; a.dv_st = dv.stride_t; a.dv_sh = dv.stride_h;
   a.kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
   a.vrows = reinterpret_cast<pisa::bf16x8*>(base + w.vrows);
-  a.kcols = reinterpret_cast<pisa::bf16x8*>(base + w.kcols);
   a.tok = base + w.tok;
   a.rank = reinterpret_cast<int32_t*>(base + w.rank);
   a.hist = reinterpret_cast<int32_t*>(base + w.hist);

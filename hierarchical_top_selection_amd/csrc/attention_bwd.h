@@ -40,7 +40,6 @@ struct BwdArgs {
   // workspace
   bf16x8* kpack;         // K rows (attention K layout)
   bf16x8* vrows;         // V rows in the K layout
-  bf16x8* kcols;         // K in the V^T layout
   char* tok;
   int32_t* rank;
   int32_t* hist;

@@ -12,8 +12,9 @@
 // * dq, query-major: one wave per (b, kvh, token), the group's heads as the 16 MFMA
 //   columns, exactly the shape of the forward kernel.  Per selected block it forms
 //   S^T = K Q^T and dP^T = V dO^T from packed key-major rows, rescales with the saved row
-//   LSE (no online softmax: P is final), and accumulates dq^T += K^T dS^T from K packed in
-//   the value layout, so the lane's own dS^T values are the B fragment.
+//   LSE (no online softmax: P is final), and accumulates dq^T += K^T dS^T with the lane's own
+//   dS^T values as the B fragment.  K^T comes from the K rows already in registers: an MFMA
+//   against a 0/1 selector puts the keys on the result rows, in the order dS^T uses.
 // * dk and dv, key-major: a deterministic inverse of the selection lists each block's
 //   tokens in ascending order (a stable counting sort: per-chunk occurrence ranks, a
 //   per-block scan over chunks, one scan over blocks, a scatter).  A work item is up to
@@ -21,7 +22,8 @@
 //   (bf16 query and output-gradient rows and row statistics, written once per token by a
 //   packing pass) into LDS, double-buffered, form S = Q K^T and dP = dO V^T
 //   with the heads as rows, and accumulate dv^T += dO^T P and dk^T += Q^T dS on the
-//   16x16x16 MFMA, whose contraction runs over the 16 head rows.  Items write partial
+//   16x16x16 MFMA, whose contraction runs over the 16 head rows; dO^T and Q^T come from
+//   the row fragments by selector MFMAs.  Items write partial
 //   sums; a last pass adds each block's partials in item order.  No atomics anywhere, so
 //   repeated calls give identical bits.
 #include "attention_bwd.h"
@@ -251,7 +253,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int64_t blk = (int64_t)bh * m1 * (kLeaf * D / 8);
   const bf16x8* krow = a.kpack + blk + lane;
   const bf16x8* vrow = a.vrows + blk + lane;
-  const bf16x8* kcol = a.kcols + blk + lane;
+  // 0/1 selector B fragments: for half h of a 32-wide k-step, column c picks k = 16 h + c, so an
+  // MFMA of a K-row fragment with sel[h] yields those 16 key columns with the keys on the result
+  // rows: K transposed, exactly (products with 1 and 0, fp32 sums).
+  bf16x8 sel[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[h][e] = (__bf16)(8 * g + e == 16 * h + col ? 1.f : 0.f);
   const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
   uint64_t rest = __ballot(slot_in_use(my_sel, lane, a.top_k, t));
 
@@ -265,15 +274,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const int64_t first = (int64_t)leaf * kLeaf;
     const int64_t off = (int64_t)leaf * (kLeaf * D / 8);
     floatx4 s_acc[4], p_acc[4];
+    Frag kf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      Frag kf, vf;
+      Frag vf;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        kf.v[s] = krow[off + (mt * (D / 32) + s) * 64];
+        kf[mt].v[s] = krow[off + (mt * (D / 32) + s) * 64];
         vf.v[s] = vrow[off + (mt * (D / 32) + s) * 64];
       }
-      s_acc[mt] = mma(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
+      s_acc[mt] = mma(kf[mt], qf, floatx4{0.f, 0.f, 0.f, 0.f});
       p_acc[mt] = mma(vf, df, floatx4{0.f, 0.f, 0.f, 0.f});
     }
     // s_acc[mt][r]: key first + perm_key(mt, 4 g + r) = first + 32 (mt / 2) + 8 g + 4 (mt % 2) + r
@@ -288,10 +298,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s_acc[mt][r], c2, -st.x));
         db[mt >> 1][4 * (mt & 1) + r] = (__bf16)(p * (p_acc[mt][r] - st.y));
       }
+    // dq^T += K^T dS^T.  The A fragment of key half kb and d tile dt holds, in lane (g, col), element
+    // e: K[first + perm_key(2 kb + e / 4, 4 g + e % 4)][16 dt + col], the key order of db[kb].
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      dq[dt] = mfma_bf16(kcol[off + dt * 64], db[0], dq[dt]);
-      dq[dt] = mfma_bf16(kcol[off + (D / 16 + dt) * 64], db[1], dq[dt]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const floatx4 lo = mfma_bf16(kf[2 * kb].v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 hi = mfma_bf16(kf[2 * kb + 1].v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
+        bf16x8 kt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          kt[r] = (__bf16)lo[r];
+          kt[4 + r] = (__bf16)hi[r];
+        }
+        dq[dt] = mfma_bf16(kt, db[kb], dq[dt]);
+      }
     }
   }
   if (col < a.group) {
@@ -380,6 +402,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
     dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale * kLog2e;
+  bf16x8 sel[2];                                        // 0/1 selectors, as in the dq pass
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[h][e] = (__bf16)(8 * g + e == 16 * h + col ? 1.f : 0.f);
 
   fetch(0);
   store(0, 0);
@@ -388,22 +415,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
     const bool more = base + kTok < len;
     if (more) fetch(base + kTok);                       // next round's records in flight
     const int nt = min(kTok, len - base);
-    // S and dP of the round's first token, then per token: P and dS, the next token's S and dP
-    // (independent work the scheduler can overlap), this token's dv and dk products.
-    FragBF16<D> qa, da;                                 // A fragments: head col, d k-slices
-    auto load_rows = [&](const Tok& tk) {
+    for (int tb = 0; tb < nt; ++tb) {
+      const Tok& tk = s_tok[buf][tb];
+      const int t = s_list[base + tb];
+      FragBF16<D> qa, da;                               // A fragments: head col, d k-slices
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         qa.v[s] = *reinterpret_cast<const bf16x8*>(&tk.q[col][32 * s + 8 * g]);
         da.v[s] = *reinterpret_cast<const bf16x8*>(&tk.dout[col][32 * s + 8 * g]);
       }
-    };
-    load_rows(s_tok[buf][0]);
-    floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});           // [head 4 g + r][key col]
-    floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
-    for (int tb = 0; tb < nt; ++tb) {
-      const Tok& tk = s_tok[buf][tb];
-      const int t = s_list[base + tb];
+      const floatx4 sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});    // [head 4 g + r][key col]
+      const floatx4 pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
       bf16x4 pb, db;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -412,18 +434,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
         pb[r] = (__bf16)p;
         db[r] = (__bf16)(p * (pacc[r] - sr.y));
       }
-      if (tb + 1 < nt) {
-        load_rows(s_tok[buf][tb + 1]);
-        sacc = mma(qa, kb, floatx4{0.f, 0.f, 0.f, 0.f});
-        pacc = mma(da, vb, floatx4{0.f, 0.f, 0.f, 0.f});
-      }
+      // A fragments of d tile dt (lane (g, col): heads 4 g + r of d column 16 dt + col) from the row
+      // fragments by a selector MFMA, which puts the heads on the result rows
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        bf16x4 doa, qta;                                // A fragments: d row 16 dt + col, heads 4 g + r
+        const floatx4 tdo = mfma_bf16(da.v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 tq = mfma_bf16(qa.v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
+        bf16x4 doa, qta;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          doa[r] = tk.dout[4 * g + r][16 * dt + col];
-          qta[r] = tk.q[4 * g + r][16 * dt + col];
+          doa[r] = (__bf16)tdo[r];
+          qta[r] = (__bf16)tq[r];
         }
         dv[dt] = mfma_k16(doa, pb, dv[dt]);                // [d 16 dt + 4 g + r][key col]
         dk[dt] = mfma_k16(qta, db, dk[dt]);
@@ -487,9 +508,8 @@ hipError_t launch_attention_bwd_t(const BwdArgs& a, hipStream_t s) {
   p.kpack = a.kpack; p.vpack = nullptr;
   p.batch = a.batch; p.n_kv_heads = a.n_kv_heads; p.head_dim = D; p.n = a.n;
   if ((e = launch_pack(p, s)) != hipSuccess) return e;
-  p.k = a.v; p.k_sb = a.v_sb; p.k_st = a.v_st; p.k_sh = a.v_sh;      // V rows, K in the value layout
-  p.v = a.k; p.v_sb = a.k_sb; p.v_st = a.k_st; p.v_sh = a.k_sh;
-  p.kpack = a.vrows; p.vpack = a.kcols;
+  p.k = a.v; p.k_sb = a.v_sb; p.k_st = a.v_st; p.k_sh = a.v_sh;      // V rows in the same key order
+  p.kpack = a.vrows;
   if ((e = launch_pack(p, s)) != hipSuccess) return e;
 
   const dim3 tok_grid(ceil_div(a.n, 4), bhs);

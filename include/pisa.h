@@ -202,7 +202,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by pisa_sparse_attn_bwd for cfg (0 for an unsupported
- * cfg): packed copies of K and V (3 * B * H_kv * ceil(N / 64) * 64 * d * 2
+ * cfg): packed copies of K and V (2 * B * H_kv * ceil(N / 64) * 64 * d * 2
  * bytes), a record per token and KV head (its queries and upstream gradients
  * in bf16 and row statistics: 8320 bytes at d = 128, 4224 at d = 64), the
  * inverse of the selection lists, and per-item
