@@ -26,6 +26,8 @@
 //   the row fragments by selector MFMAs.  Items write partial
 //   sums; a last pass adds each block's partials in item order.  No atomics anywhere, so
 //   repeated calls give identical bits.
+#include <type_traits>
+
 #include "attention_bwd.h"
 
 namespace pisa {
@@ -33,6 +35,7 @@ namespace pisa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline floatx4 mfma_k16(bf16x4 a, bf16x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -46,6 +49,15 @@ __device__ inline bf16x8 load8_bf16(const float* p) {
   r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
   r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
   return r;
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
 }
 
 // Lane < K holds slot `lane` of the token's selection; true for entries that take part:
@@ -360,31 +372,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
 
   // Round r stages tokens [kTok r, kTok r + kTok) of the item: piece c of a record goes to row
   // c / (D / 8) of q (c < 16 D / 8), of dO, or to the statistics.
-  uint4 stage[kPer];
-  auto fetch = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int x = threadIdx.x + 256 * i;
-      const int tb = x / kPieces, c = x % kPieces;
-      if (x < kTok * kPieces && base + tb < len)
-        stage[i] = reinterpret_cast<const uint4*>(records + (int64_t)s_list[base + tb] * kRec)[c];
-    }
+  u32x4 stage[kPer];                                    // a native vector type: kept in registers
+  auto fetch = [&](int base) __attribute__((always_inline)) {   // base < len
+    // unconditional loads (a piece past the round re-reads a valid one and is not stored): a
+    // guarded load would be waited for where its branch joins
+    const int last = min(kTok, len - base) - 1;
+    static_for<kPer>([&](auto I) {
+      const int x = threadIdx.x + 256 * I();
+      const int tb = min(x / kPieces, last), c = x % kPieces;
+      stage[I()] = reinterpret_cast<const u32x4*>(records + (int64_t)s_list[base + tb] * kRec)[c];
+    });
   };
-  auto store = [&](int buf, int base) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int x = threadIdx.x + 256 * i;
+  auto store = [&](int buf, int base) __attribute__((always_inline)) {
+    // piece c: row c / (d / 8) of q (rows 0-15) or dO (rows 16-31), or the statistics
+    static_for<kPer>([&](auto I) {
+      const int x = threadIdx.x + 256 * I();
       const int tb = x / kPieces, c = x % kPieces;
-      if (x < kTok * kPieces && base + tb < len) {
-        Tok& tk = s_tok[buf][tb];
-        uint4* dst;
-        if (c < 16 * kRowPieces) dst = reinterpret_cast<uint4*>(&tk.q[c / kRowPieces][8 * (c % kRowPieces)]);
-        else if (c < 32 * kRowPieces)
-          dst = reinterpret_cast<uint4*>(&tk.dout[(c - 16 * kRowPieces) / kRowPieces][8 * (c % kRowPieces)]);
-        else dst = reinterpret_cast<uint4*>(&tk.st[2 * (c - 32 * kRowPieces)]);
-        *dst = stage[i];
-      }
-    }
+      const int off = c < 32 * kRowPieces ? (c / kRowPieces) * kRow * 2 + 16 * (c % kRowPieces)
+                                          : 64 * kRow + 16 * (c - 32 * kRowPieces);
+      if (x < kTok * kPieces && base + tb < len)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(&s_tok[buf][tb]) + off) = stage[I()];
+    });
   };
 
   FragBF16<D> kb, vb;                                   // B fragments: key col, d k-slices
@@ -408,12 +416,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sel[h][e] = (__bf16)(8 * g + e == 16 * h + col ? 1.f : 0.f);
 
+  // Round r's records are fetched into registers two rounds ahead and stored to LDS at the start
+  // of round r - 1, so the loads stay in flight during a whole round of compute; the registers
+  // carry them across the loop, which also keeps the compiler from sinking the loads.
   fetch(0);
   store(0, 0);
+  if (kTok < len) fetch(kTok);
   __syncthreads();
   for (int base = 0, buf = 0; base < len; base += kTok, buf ^= 1) {
-    const bool more = base + kTok < len;
-    if (more) fetch(base + kTok);                       // next round's records in flight
+    if (base + kTok < len) store(buf ^ 1, base + kTok);      // that buffer was last read a round ago
+    if (base + 2 * kTok < len) fetch(base + 2 * kTok);
     const int nt = min(kTok, len - base);
     for (int tb = 0; tb < nt; ++tb) {
       const Tok& tk = s_tok[buf][tb];
@@ -450,7 +462,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
         dk[dt] = mfma_k16(qta, db, dk[dt]);
       }
     }
-    if (more) store(buf ^ 1, base + kTok);              // that buffer was last read a round ago
     __syncthreads();
   }
   float* pk = a.partial + (int64_t)item * 2 * kLeaf * D;
