@@ -11,6 +11,8 @@
 
 namespace pisa {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // One workgroup per (block j, b * Hkv + kvh): the block's rows are staged in LDS, then
 // every thread writes whole 16-byte pieces.
 template <int D>
@@ -28,10 +30,10 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(PackArgs a) {
     const int r = e / (D / 8), c8 = e % (D / 8);
     const int64_t key = first + r;
     const bool in = key < a.n;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&ks[r][8 * c8]) = in ? *reinterpret_cast<const uint4*>(kbase + key * a.k_st + 8 * c8) : zero;
+    const u32x4 zero = {0u, 0u, 0u, 0u};         // native vector type: stays in registers
+    *reinterpret_cast<u32x4*>(&ks[r][8 * c8]) = in ? *reinterpret_cast<const u32x4*>(kbase + key * a.k_st + 8 * c8) : zero;
     if (with_v)
-      *reinterpret_cast<uint4*>(&vs[r][8 * c8]) = in ? *reinterpret_cast<const uint4*>(vbase + key * a.v_st + 8 * c8) : zero;
+      *reinterpret_cast<u32x4*>(&vs[r][8 * c8]) = in ? *reinterpret_cast<const u32x4*>(vbase + key * a.v_st + 8 * c8) : zero;
   }
   __syncthreads();
   const int m1 = ceil_div(a.n, kLeaf);
