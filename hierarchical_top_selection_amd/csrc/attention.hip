@@ -58,8 +58,7 @@ __device__ inline float softmax_block(floatx4 (&acc)[4], float c2, bool mask, in
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[mt][r]);
-  tmax = wave_max_xor(tmax, 16);
-  tmax = wave_max_xor(tmax, 32);
+  tmax = rows_max(tmax);
   const float m_new = fmaxf(m_run, tmax * c2);
   const float m_use = m_new == kNegInf ? 0.f : m_new;
   const float alpha = exp2f(m_run - m_use);
@@ -72,8 +71,7 @@ __device__ inline float softmax_block(floatx4 (&acc)[4], float c2, bool mask, in
       acc[mt][r] = p;
       psum += p;
     }
-  psum = wave_add_xor(psum, 16);
-  psum = wave_add_xor(psum, 32);
+  psum = rows_sum(psum);
   l_run = l_run * alpha + psum;
   m_run = m_new;
   return alpha;
@@ -98,7 +96,7 @@ __device__ inline void finish_row(const AttnArgs& a, const floatx4* o, int nd16,
 template <typename TO, int D>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   typedef FragBF16<D> Frag;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
   const int bh = blockIdx.y;
@@ -180,8 +178,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[mt][r]);
-    tmax = wave_max_xor(tmax, 16);
-    tmax = wave_max_xor(tmax, 32);
+    tmax = rows_max(tmax);
     const float m_new = fmaxf(m_run, tmax * c2);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // arguments <= 0: no range fix-up needed
@@ -195,8 +192,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
         psum += p;
         pb[mt >> 1][4 * (mt & 1) + r] = (__bf16)p;      // k-index 4 h + r of key half kb = mt / 2
       }
-    psum = wave_add_xor(psum, 16);
-    psum = wave_add_xor(psum, 32);
+    psum = rows_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
@@ -220,7 +216,7 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
   constexpr int kRowVecs = D / 4;
   __shared__ __align__(16) float vstage[4][kChunk][D + kPad];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
   const int bh = blockIdx.y;

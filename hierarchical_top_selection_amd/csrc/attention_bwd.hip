@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void bwd_scatter_kernel(BwdArgs a, int chunks)
 template <typename TD, int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef FragBF16<D> Frag;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
   const int bh = blockIdx.y;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int len = min(kBwdItem, a.seg_len[e] - start);
   const int32_t* toks = a.list + a.seg_base[e] + start;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 4, col = lane & 15;
   const int key = j * kLeaf + 16 * wave + col;          // this lane's key column
   const char* records = a.tok + (int64_t)bh * a.n * kRec;

@@ -208,15 +208,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
           acc[mt][r] = z;
           m = fmaxf(m, z);
         }
-      m = wave_max_xor(m, 16);
-      m = wave_max_xor(m, 32);
+      m = rows_max(m);
       float sum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(acc[mt][r] - m);   // key t is valid: m finite
-      sum = wave_add_xor(sum, 16);
-      sum = wave_add_xor(sum, 32);
+      sum = rows_sum(sum);
       head = m + __builtin_amdgcn_logf(sum);
     } else {                                            // mean, or mean + var / 2, natural units
       const float cnt = (float)min(kLeaf, t - first + 1);
@@ -230,8 +228,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
           if (head_ok) zl[(slot * kLeaf + key) * G + col] = ok ? acc[mt][r] * c2 : kNegInf;
           s1 += ok ? acc[mt][r] : 0.f;
         }
-      s1 = wave_add_xor(s1, 16);
-      s1 = wave_add_xor(s1, 32);
+      s1 = rows_sum(s1);
       const float mean = s1 / cnt;
       head = mean * a.scale;
       if (a.score == 2) {
@@ -243,8 +240,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
             const float dv = (acc[mt][r] - mean) * a.scale;
             s2 += first + 16 * mt + 4 * g + r <= t ? dv * dv : 0.f;
           }
-        s2 = wave_add_xor(s2, 16);
-        s2 = wave_add_xor(s2, 32);
+        s2 = rows_sum(s2);
         head += 0.5f * s2 / cnt;
       }
     }

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void flat_kpack_kernel(FlatArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void flat_select_kernel(FlatArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int grp = blockIdx.x * 4 + wave;                               // 16-token group
   const int t0 = 16 * grp;
   if (t0 >= a.n) return;

@@ -9,10 +9,11 @@
 // bf16 inputs read both from packed copies (K blocks with keys in perm_key order,
 // query groups; pack.hip) so every fragment load is one contiguous run.  The product is kept transposed, S^T = K Q^T
 // (keys on rows, heads on columns), so a lane owns 16 keys of one head: the
-// per-head max and sum over the 64 keys are in-lane plus two cross-group
-// shuffles, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
+// per-head max and sum over the 64 keys are in-lane plus two row-swap
+// permutes across the lane groups, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
 // 16-lane reduction; one lane writes the pair's score.  The mean and mean + var/2 score
-// variants (PISA-1 / PISA-2) reduce the same logits to their mean and variance instead.  bf16 inputs use
+// variants (PISA-1 / PISA-2) reduce the same logits to their mean and variance instead; the
+// score is a template parameter, so each instantiation carries only its own reduction.  bf16 inputs use
 // v_mfma_f32_16x16x32_bf16 (exact products, fp32 sums); fp32 inputs
 // v_mfma_f32_16x16x4_f32.
 #include "kernels.h"
@@ -24,8 +25,10 @@ namespace pisa {
 constexpr int kXcds = 8;
 
 constexpr int kItemsPerWave = 4;
+// a wave's pairs fit two registers per lane, and its items the four-way picks below
+static_assert(kItemsPerWave <= 4 && kItemsPerWave * kPairsPerItem <= 128, "wave pair stream too long");
 
-template <typename T, int D>
+template <typename T, int D, int kScore>
 __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], const typename RawFrag<T, D>::type& qf,
                                  int packed, const LeafArgs& a, int start, int last, float c2, bool head_ok,
                                  int g, int lane, float* uout) {
@@ -44,7 +47,7 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
   };
   const int lim = min(t - start, last);
   float head;                                           // this head's score, natural units
-  if (a.score == 0) {                                   // LSE
+  if constexpr (kScore == 0) {                          // LSE
     if (lim < kLeaf - 1) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -57,16 +60,14 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][r]);
-    m = wave_max_xor(m, 16);
-    m = wave_max_xor(m, 32);
+    m = rows_max(m);
     const float mc = m * c2;
     float s = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
-    s = wave_add_xor(s, 16);
-    s = wave_add_xor(s, 32);
+    s = rows_sum(s);
     // natural-log LSE: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
     head = (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f;
   } else {                                              // mean, or mean + var / 2, of the valid logits
@@ -76,11 +77,10 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) s1 += key_off(mt, r) <= lim ? acc[mt][r] : 0.f;
-    s1 = wave_add_xor(s1, 16);
-    s1 = wave_add_xor(s1, 32);
+    s1 = rows_sum(s1);
     const float mean = s1 / cnt;                        // of the raw dot products
     head = mean * a.scale;
-    if (a.score == 2) {
+    if constexpr (kScore == 2) {
       float s2 = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -89,8 +89,7 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
           const float dv = (acc[mt][r] - mean) * a.scale;
           s2 += key_off(mt, r) <= lim ? dv * dv : 0.f;
         }
-      s2 = wave_add_xor(s2, 16);
-      s2 = wave_add_xor(s2, 32);
+      s2 = rows_sum(s2);
       head += 0.5f * s2 / cnt;
     }
   }
@@ -98,14 +97,14 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
   if (lane == 15) uout[(int64_t)t * a.width + slot] = u;   // the group's head sum (row 0)
 }
 
-// Each wave walks kItemsPerWave consecutive items of one window.  The next item's
-// record and query list are fetched one item ahead, the query rows one query ahead
-// (across item boundaries), and consecutive items of the same leaf keep their keys.
+// Each wave walks kItemsPerWave consecutive items of one window as one stream of pairs:
+// the query rows are fetched two pairs ahead (across item boundaries), and consecutive
+// items of the same leaf keep their keys.
 // fp32 keys at d = 128 need 128 VGPRs of fragments: no occupancy target there.
-template <typename T, int D, int kWaves = (sizeof(T) == 4 && D == 128) ? 1 : 3>
+template <typename T, int D, int kScore, int kWaves = (sizeof(T) == 4 && D == 128) ? 1 : 3>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) void leaf_lse_kernel(LeafArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int blocks_per_window = ceil_div(a.item_cap, 4 * kItemsPerWave);
   const int xcd = blockIdx.x % kXcds, slot_id = blockIdx.x / kXcds;
   const int64_t wid = (int64_t)kXcds * (slot_id / blocks_per_window) + xcd;   // bh * n_windows + w
@@ -119,21 +118,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
   const int2* items = a.items + wid * a.item_cap;
   const int32_t* pairs = a.pairs + ((int64_t)bh * a.n + (int64_t)w * a.window) * a.width;
   const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.k_sb + kvh * a.k_sh;
-  const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)(kvh * a.group + col) * a.q_sh;
   float* uout = a.leaf_u + (int64_t)bh * a.n * a.width;
   const float c2 = a.scale * 1.4426950408889634f;      // logits in base-2 units
   const bool head_ok = col < a.group;
 
-  auto item_pairs = [&](int2 rec) {
-    const int np = rec.y >> 20, p0 = rec.y & 0xfffff;
-    return lane < np ? pairs[p0 + lane] : 0;
-  };
   const int64_t qp_token = (int64_t)a.group * D / 8;                  // packed query pieces per token
-  const bf16x8* qpack = a.qpack + (int64_t)bh * a.n * qp_token + g * a.group + col;
+  // Lanes of head columns >= G read column 0's rows instead (finite values; those columns never
+  // reach the head sum), so every query load is unconditional and the compiler's wait counts
+  // stay exact across the look-ahead below.
+  const int qcol = head_ok ? col : 0;
+  const bf16x8* qpack = a.qpack + (int64_t)bh * a.n * qp_token + g * a.group + qcol;
+  const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)(kvh * a.group + qcol) * a.q_sh;
   auto load_q = [&](Frag& f, int packed) {
-    if (!head_ok) {
-      f.zero();
-    } else if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2) {
       const bf16x8* p = qpack + (int64_t)(packed >> 6) * qp_token;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) f.v[s] = p[4 * s * a.group];
@@ -142,49 +139,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
     }
   };
 
-  int2 rec = items[it0];
-  int2 rec_n = it0 + 1 < it_end ? items[it0 + 1] : make_int2(-1, 0);
-  int pr = item_pairs(rec);
-  int pr_n = it0 + 1 < it_end ? item_pairs(rec_n) : 0;
+  // The wave's items (at most kItemsPerWave, each 1..kPairsPerItem pairs) as one flat stream of
+  // pairs: item j's record in lane j, its pairs at flat positions [off_j, off_j + count_j); lane l
+  // holds the pairs at flat positions l and l + 64.
+  const int nit = it_end - it0;
+  const int2 myrec = lane < nit ? items[it0 + lane] : make_int2(0, 0);
+  const int cnt0 = __builtin_amdgcn_readlane(myrec.y >> 20, 0), cnt1 = __builtin_amdgcn_readlane(myrec.y >> 20, 1);
+  const int cnt2 = __builtin_amdgcn_readlane(myrec.y >> 20, 2), cnt3 = __builtin_amdgcn_readlane(myrec.y >> 20, 3);
+  const int off1 = cnt0, off2 = off1 + cnt1, off3 = off2 + cnt2;
+  const int total = __builtin_amdgcn_readfirstlane(off3 + cnt3);
+  auto pick = [](int j, int v0, int v1, int v2, int v3) { return j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3; };
+  const int p00 = __builtin_amdgcn_readlane(myrec.y & 0xfffff, 0), p01 = __builtin_amdgcn_readlane(myrec.y & 0xfffff, 1);
+  const int p02 = __builtin_amdgcn_readlane(myrec.y & 0xfffff, 2), p03 = __builtin_amdgcn_readlane(myrec.y & 0xfffff, 3);
+  auto flat_pair = [&](int f) {
+    if (f >= total) return 0;
+    const int j = (f >= off1) + (f >= off2) + (f >= off3);
+    return pairs[pick(j, p00, p01, p02, p03) + f - pick(j, 0, off1, off2, off3)];
+  };
+  const int fl0 = flat_pair(lane), fl1 = flat_pair(lane + 64);
+  auto pair_at = [&](int f) {                          // f is wave-uniform: a scalar read
+    return f < 64 ? __builtin_amdgcn_readlane(fl0, f) : __builtin_amdgcn_readlane(fl1, f - 64);
+  };
+  const int leaf0 = __builtin_amdgcn_readlane(myrec.x, 0), leaf1 = __builtin_amdgcn_readlane(myrec.x, 1);
+  const int leaf2 = __builtin_amdgcn_readlane(myrec.x, 2), leaf3 = __builtin_amdgcn_readlane(myrec.x, 3);
+
   Frag kf[4];
-  int cur_leaf = -1;
-  Frag q0, q1;
-  load_q(q0, __builtin_amdgcn_readfirstlane(pr));
-  for (int it = it0; it < it_end; ++it) {
-    const int leaf = rec.x, np = rec.y >> 20;
-    const int2 rec_nn = it + 2 < it_end ? items[it + 2] : make_int2(-1, 0);
-    if (leaf != cur_leaf) {                            // rows past the end are zero or clamped, then masked
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8* blk = a.kpack + ((int64_t)bh * a.n_leaves + leaf) * (kLeaf * D / 8) + lane;
+  int cur_leaf = -1, start = 0, last = 0;
+  int next_item = 0, next_start = 0;                   // the next item to enter and its first flat position
+  // Query rows are fetched two pairs ahead through a ring of three fragments (static slots, so
+  // the ring stays in registers).  At an item boundary the keys are requested before the
+  // look-ahead query, so the wait for them does not include it.
+  auto step = [&](int f, Frag& cur, Frag& fill) {
+    if (f == next_start) {
+      const int leaf = __builtin_amdgcn_readfirstlane(pick(next_item, leaf0, leaf1, leaf2, leaf3));
+      if (leaf != cur_leaf) {                          // rows past the end are zero or clamped, then masked
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8* blk = a.kpack + ((int64_t)bh * a.n_leaves + leaf) * (kLeaf * D / 8) + lane;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int s = 0; s < D / 32; ++s) kf[mt].v[s] = blk[(mt * (D / 32) + s) * 64];
-      } else {
-        const int64_t first = (int64_t)leaf * kLeaf;
+            for (int s = 0; s < D / 32; ++s) kf[mt].v[s] = blk[(mt * (D / 32) + s) * 64];
+        } else {
+          const int64_t first = (int64_t)leaf * kLeaf;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+          for (int mt = 0; mt < 4; ++mt) kf[mt].load(kbase + min(first + 16 * mt + col, (int64_t)a.n - 1) * a.k_st, g);
+        }
+        cur_leaf = leaf;
       }
-      cur_leaf = leaf;
+      start = leaf * kLeaf;
+      last = min(kLeaf - 1, a.n - 1 - start);          // last key of this leaf, relative to its start
+      ++next_item;
+      next_start = __builtin_amdgcn_readfirstlane(next_item < nit ? pick(next_item, 0, off1, off2, off3) : total);
     }
-    const int start = leaf * kLeaf;
-    const int last = min(kLeaf - 1, a.n - 1 - start);   // last key of this leaf, relative to its start
-    for (int i = 0; i < np; ++i) {
-      // rows of the following query (this item's next, or the next item's first)
-      const bool in_item = i + 1 < np;
-      const bool have_next = in_item || it + 1 < it_end;
-      // lane broadcasts of the uniform pair index: scalar reads, no LDS round trip
-      const int nxt = in_item ? __builtin_amdgcn_readlane(pr, i + 1) : __builtin_amdgcn_readfirstlane(pr_n);
-      if (have_next) load_q(q1, nxt);
-      leaf_pair<T, D>(kf, q0, __builtin_amdgcn_readlane(pr, i), a, start, last, c2, head_ok, g, lane, uout);
-      q0 = q1;
-    }
-    if (it + 1 < it_end) {
-      rec = rec_n;
-      pr = pr_n;
-      rec_n = rec_nn;
-      pr_n = it + 2 < it_end ? item_pairs(rec_n) : 0;
-    }
+    load_q(fill, pair_at(min(f + 2, total - 1)));     // past the end: a repeat, never used
+    leaf_pair<T, D, kScore>(kf, cur, pair_at(f), a, start, last, c2, head_ok, g, lane, uout);
+  };
+  Frag qa, qb, qc;
+  load_q(qa, pair_at(0));
+  load_q(qb, pair_at(min(1, total - 1)));
+  for (int f = 0; f < total; f += 3) {
+    step(f, qa, qc);
+    if (f + 1 < total) step(f + 1, qb, qa);
+    if (f + 2 < total) step(f + 2, qc, qb);
   }
 }
 
@@ -192,7 +208,13 @@ template <typename T, int D>
 hipError_t launch_leaf_t(const LeafArgs& a, hipStream_t s) {
   const int64_t windows = (int64_t)a.batch * a.n_kv_heads * a.n_windows;
   const int64_t blocks = kXcds * ((windows + kXcds - 1) / kXcds) * ceil_div(a.item_cap, 4 * kItemsPerWave);
-  hipLaunchKernelGGL((leaf_lse_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)blocks);
+  if (a.score == 1)
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 1>), grid, dim3(256), 0, s, a);
+  else if (a.score == 2)
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -143,9 +143,46 @@ template <typename T, int D> struct RawFrag;
 template <int D> struct RawFrag<float, D> { typedef FragF32<D> type; };
 template <int D> struct RawFrag<__bf16, D> { typedef FragBF16<D> type; };
 
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot tell that threadIdx.x / 64 is uniform, and everything derived from it
+// (token, item and loop bounds) would otherwise live in vector registers and take
+// exec-masked branches.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ----------------------------------------------------------------------------- wave reductions
 __device__ inline float wave_max_xor(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask, 64)); }
 __device__ inline float wave_add_xor(float x, int mask) { return x + __shfl_xor(x, mask, 64); }
+
+// Max / sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48), every lane getting the
+// result, with the gfx950 row-swap permutes instead of LDS shuffles.  With both operands equal to
+// x, v_permlane16_swap leaves rows (r0, r0, r2, r2) in the first and (r1, r1, r3, r3) in the
+// second register, v_permlane32_swap the low half twice and the high half twice.  Sums come out
+// as (r0 + r1) + (r2 + r3) in every lane, the order of the xor-shuffle pair above.  The permutes
+// are written in asm because the compiler folds the two results of its builtins into one when
+// the operands are the same value; a permute reads its registers two wait states after the VALU
+// write, hence the s_nop on each side.
+__device__ inline void swap_rows16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap_rows32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ inline float rows_max(float x) {
+  float a = x, b = x;
+  swap_rows16(a, b);
+  a = fmaxf(a, b);
+  b = a;
+  swap_rows32(a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float rows_sum(float x) {
+  float a = x, b = x;
+  swap_rows16(a, b);
+  a = a + b;
+  b = a;
+  swap_rows32(a, b);
+  return a + b;
+}
 
 // Sum over the 16 lanes of each row (lanes 16 r .. 16 r + 15) with DPP row shifts;
 // the row total lands in the row's last lane (lane 16 r + 15).

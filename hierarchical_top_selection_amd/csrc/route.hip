@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
 // kScore: the candidate score (pisa_score), fixed per instantiation so only its code is live.
 template <typename T, int D, int kScore>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
   const int bh = blockIdx.y;

@@ -10,7 +10,7 @@
 namespace pisa {
 
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.n) return;
   const int64_t row = (int64_t)blockIdx.y * a.n + t;
