@@ -59,7 +59,8 @@ template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 rem
     // tile rows 2 i, 2 i + 1 are the two children of one candidate, so each fragment
     // load covers whole 128-byte lines of the pair blocks
     __device__ inline void load(const RouteArgs& a, const Row* rows, int li, int child, int g) {
-      const Row* r = rows + (a.pair_off[li] + (child >> 1)) * (4 * D) + 32 * (child & 1) + 8 * g;
+      // uniform level base plus a 32-bit per-lane offset (a level's pair blocks span far less than 4 GB)
+      const Row* r = rows + a.pair_off[li] * (4 * D) + (uint32_t)((child >> 1) * (4 * D) + 32 * (child & 1) + 8 * g);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         h.v[s] = *reinterpret_cast<const bf16x8*>(r + 64 * s);
@@ -166,7 +167,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
     bool keep = cand >= 0;
     if (n_valid > a.top_k) {
       const int span = 64 - __clzll(valid);            // highest occupied lane + 1
-      const int tiles = (2 * span + 15) / 16;
+      // an even tile count, so the double-buffered loop below has no conditional half; a padding
+      // tile only scores empty candidate lanes, whose keys are 0
+      const int tiles = (((2 * span + 15) / 16) + 1) & ~1;
       // child of tile nt owned by this lane's row index: candidate slot/2, child slot&1.  Rows of
       // invalid children load a clamped row and are masked.
       auto child_of = [&](int nt, bool& ok) {
@@ -177,25 +180,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         return ok ? child : 0;
       };
       float u = kNegInf;                               // score of candidate `lane` (base 2)
-      bool ok_n;
-      int child_n = child_of(0, ok_n);
-      typename Ops::Tile kf_n;
-      kf_n.load(a, rows, level - 2, child_n, g);
-      for (int nt = 0; nt < tiles; ++nt) {
-        const typename Ops::Tile kf = kf_n;
-        // validity of the children this lane holds results for: rows 4g .. 4g+3 of the tile
-        const uint64_t okmask = __ballot(ok_n);
-        if (nt + 1 < tiles) {                          // next tile's rows in flight during this one
-          child_n = child_of(nt + 1, ok_n);
-          kf_n.load(a, rows, level - 2, child_n, g);
-        }
+      // Tiles are double-buffered without copies: tile nt computes from `cur` while tile nt + 1's
+      // rows are requested into `nxt` (the last tile requests its own rows again, so every load
+      // is unconditional).  The compiler may still sink those loads below the products to save
+      // registers; pinning them with a scheduling barrier measured slower (3.2 -> 3.85 ms at
+      // N = 262144), so they are left to it.
+      auto do_tile = [&](int nt, typename Ops::Tile& cur, typename Ops::Tile& nxt, bool& ok_cur) {
+        // rows 4g .. 4g+3 of the tile hold this lane's results: bits 4g .. 4g+3 of the ballot.  A
+        // candidate's first child is valid whenever the candidate is (its first key is the
+        // candidate's own), so only the second child of each pair is tested; padding candidates
+        // score finite garbage and never rank (their key is 0).
+        const uint32_t rows_ok = (uint32_t)__ballot(ok_cur) >> (4 * g);
+        bool ok_n;
+        const int child_n = child_of(min(nt + 1, tiles - 1), ok_n);
+        nxt.load(a, rows, level - 2, child_n, g);
+        ok_cur = ok_n;
         // S^T tile: rows = 16 children, columns = heads; lane (g, col) gets children 4g + i of head col
-        const floatx4 acc = Ops::dot(kf, qf);
+        const floatx4 acc = Ops::dot(cur, qf);
         float pscore[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {                  // candidate 8 nt + 2g + h: children rows 4g + 2h, +1
-          const int r0 = 4 * g + 2 * h;
-          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], (okmask >> r0) & 1, (okmask >> (r0 + 1)) & 1,
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u,
                                       kScore, a.scale, c2);
           pscore[h] = row_sum_to_last(col < a.group ? sc : 0.f);   // sum over the group's heads
         }
@@ -204,6 +209,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         const float s0 = __shfl(pscore[0], src, 64);
         const float s1 = __shfl(pscore[1], src, 64);
         if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
+      };
+      bool ok_t;
+      typename Ops::Tile ta, tb;
+      ta.load(a, rows, level - 2, child_of(0, ok_t), g);
+      for (int nt = 0; nt < tiles; nt += 2) {
+        do_tile(nt, ta, tb, ok_t);
+        do_tile(nt + 1, tb, ta, ok_t);
       }
       // exact rank among the candidates by (score descending, index ascending), as one 64-bit key:
       // the score's bits made order-preserving above the complemented index; empty lanes are 0,
