@@ -377,10 +377,10 @@ TRAFFIC_SOURCES = ("attention.hip", "kernels.h", "pisa_device.h")
 
 
 def attention_traffic(workload: str):
-    """HBM-side bytes per attention launch (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
+    """HBM-side bytes per attention call, both passes (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
     if workload != "prefill_n262144" or not os.path.exists(TRAFFIC_FILE):
         return None
-    fields = dict(re.findall(r"^(source_sha256|fetch_bytes_per_launch|write_bytes_per_launch): (\S+)\s*$",
+    fields = dict(re.findall(r"^(source_sha256|fetch_bytes_per_call|write_bytes_per_call): (\S+)\s*$",
                              open(TRAFFIC_FILE).read(), re.M))
     h = hashlib.sha256()
     for name in TRAFFIC_SOURCES:
@@ -388,7 +388,7 @@ def attention_traffic(workload: str):
             h.update(f.read())
     if len(fields) != 3 or h.hexdigest() != fields["source_sha256"]:
         return None
-    return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    return int(fields["fetch_bytes_per_call"]) + int(fields["write_bytes_per_call"])
 
 
 def main() -> int:
@@ -474,9 +474,12 @@ def main() -> int:
         "pyramid_ms": main_run["pyramid_ms"],
         "select_ms": main_run["select_ms"],
         "attn_ms": main_run["attn_ms"],
-        # attention_bf16_kernel, timed with the block packing that sparse_attn_fwd runs before it
-        # (about 0.4% of the call); flops count valid keys only
-        "roofline": {"kernel": "attention_bf16_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+        # attention_bf16_kernel: one sparse_attn_fwd call runs it twice (even, then odd block ids,
+        # for a float32 output), so achieved and traffic are per call, i.e. per pair of launches,
+        # timed with the block packing that the call runs first (about 0.5% of it); flops count
+        # valid keys only
+        "roofline": {"kernel": "attention_bf16_kernel", "launches": 2 if w.dtype == "bf16" else 1,
+                     "bound": "mfma", "achieved": attn_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": attention_traffic(w.name)},
         "cpu_baseline": cpu,
         "also": extra,

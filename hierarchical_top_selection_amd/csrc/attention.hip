@@ -17,6 +17,13 @@
 // MFMAs have consumed K_j (and the PV MFMAs V_j), the registers are refilled for
 // block j+1, so the gather latency overlaps the softmax and MFMA work.  fp32
 // inputs take a plain path that stages V through LDS, on v_mfma_f32_16x16x4_f32.
+//
+// With a float32 output the bf16 path runs in two passes, the even block ids and
+// then the odd ones.  The first pass leaves its online-softmax state (o not yet
+// normalised in the output row, the running max and sum per head in the
+// workspace) and the second resumes from it.  The softmax is order-free, so this
+// only changes the order of the fp32 sums.  Each pass gathers from half of the
+// blocks, so the hot blocks take half the L2 and more of the other reads hit it.
 #include "kernels.h"
 
 namespace pisa {
@@ -113,7 +120,8 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   const bf16x8* kpack = a.kpack + (int64_t)bh * m1 * (kLeaf * D / 8);
   const bf16x8* vpack = a.vpack + (int64_t)bh * m1 * (kLeaf * D / 8);
   const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
-  const uint64_t valid = __ballot(my_sel >= 0);        // entries < 0 are skipped
+  // entries < 0 are skipped; with several passes this one takes the blocks j % n_passes == pass
+  const uint64_t valid = __ballot(my_sel >= 0 && (a.n_passes == 1 || my_sel % a.n_passes == a.pass));
   const int nsel = __popcll(valid);
   const float c2 = a.scale * kLog2e;
 
@@ -139,6 +147,18 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
+  // float32 output row of this head (also the carried state between passes); the (m, l) pair
+  float* orow = reinterpret_cast<float*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh;
+  float* ml = a.part_ml + (((int64_t)bh * a.n + t) * a.group + col) * 2;
+  if (a.pass > 0 && col < a.group) {                   // resume the previous pass's online softmax
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const float4 x = *reinterpret_cast<const float4*>(orow + 16 * dt + 4 * g);
+      o[dt] = floatx4{x.x, x.y, x.z, x.w};
+    }
+    m_run = ml[0];
+    l_run = ml[1];
+  }
 
   uint64_t rest = valid;
   int leaf = 0;
@@ -204,7 +224,18 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     if (more) load_v(leaf_n);                          // V^T of the next block into the freed fragments
     leaf = leaf_n;
   }
-  if (col < a.group) finish_row<TO>(a, o, D / 16, m_run, l_run, b, t, head, g);
+  if (col < a.group) {
+    if (a.pass + 1 < a.n_passes) {                     // hand the state to the next pass
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) store4<float>(orow + 16 * dt + 4 * g, o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (g == 0) {
+        ml[0] = m_run;
+        ml[1] = l_run;
+      }
+    } else {
+      finish_row<TO>(a, o, D / 16, m_run, l_run, b, t, head, g);
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------- fp32, plain
@@ -289,7 +320,12 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     p.batch = a.batch; p.n_kv_heads = a.n_kv_heads; p.head_dim = D; p.n = a.n;
     hipError_t e = launch_pack(p, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, a);
+    for (int pass = 0; pass < a.n_passes; ++pass) {
+      AttnArgs ap = a;
+      ap.pass = pass;
+      hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, ap);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   } else {
     hipLaunchKernelGGL((attention_f32_kernel<TO, D>), grid, dim3(256), 0, s, a);
   }

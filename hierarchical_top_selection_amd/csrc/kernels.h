@@ -96,6 +96,12 @@ struct AttnArgs {
   float* row_lse;        // optional [B][Hq][N]
   bf16x8* kpack;         // bf16 inputs: packed K blocks (see PackArgs), workspace
   bf16x8* vpack;         // bf16 inputs: packed V blocks, workspace
+  // Passes over the selected blocks (bf16 inputs, float32 output): pass p takes the blocks j with
+  // j % n_passes == p.  A pass before the last leaves its online-softmax state in the output
+  // rows (o not yet normalised) and in part_ml ([B*Hkv][N][G] pairs (m in base-2 units, l),
+  // workspace); the next pass resumes from it.
+  int pass, n_passes;
+  float* part_ml;
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
   bool bf16;             // element type of q, k, v

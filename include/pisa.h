@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 4
+#define PISA_ABI_VERSION 5
 
 typedef enum {
   PISA_OK = 0,
@@ -178,7 +178,10 @@ pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* py
 /* Workspace bytes needed by pisa_sparse_attn_fwd for cfg: bf16 inputs stage K and
  * V as packed 64-key blocks, each fragment of the attention products one
  * contiguous run (2 * B * H_kv * ceil(N / 64) * 64 * d * 2 bytes, each half
- * rounded up to 256 bytes); fp32 inputs need none (0). */
+ * rounded up to 256 bytes), followed by B * H_q * N * 8 bytes (rounded up to
+ * 256) for the softmax state carried between the two passes of a float32-output
+ * call (even block ids, then odd ones; the output rows hold the partial sums
+ * between them); fp32 inputs need none (0). */
 size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
 
 /*

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(declared) == 15
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 4
+    assert lib.pisa_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -88,8 +88,9 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
     # output element type must be float32 or bfloat16
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 5,
                                     None, ctypes.c_void_p(4096), 1 << 30, None) == 1
-    # bf16 attention needs its V^T workspace
-    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == 2 * 4096 * 128 * 2
+    # bf16 attention needs its workspace: packed K and V blocks, then the (m, l) pair of every
+    # (token, query head) carried between the two passes of a float32-output call
+    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == 2 * 4096 * 128 * 2 + 16 * 4096 * 2 * 4
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
                                     None, None, 0, None) == 3
 
