@@ -150,6 +150,59 @@ def test_strided_inputs_match_contiguous():
     assert torch.equal(pyr, ref["pyr"]) and torch.equal(sel, ref["sel"]) and torch.equal(o, ref["o_native"])
 
 
+def _parity_selection(n: int, K: int, seed: int) -> np.ndarray:
+    """Selection rows that stress the even / odd block-id passes of the float32-output attention:
+    by t % 5, only even blocks, only odd blocks, no block at all, valid blocks with -1 holes
+    between them, and distinct blocks in random order."""
+    rng = np.random.default_rng(seed)
+    sel = np.full((n, K), -1, dtype=np.int32)
+    for t in range(n):
+        valid = np.arange(t // 64 + 1)
+        kind = t % 5
+        if kind == 0:
+            pick = valid[valid % 2 == 0][-K:]
+        elif kind == 1:
+            pick = valid[valid % 2 == 1][-K:]
+        elif kind == 2:
+            pick = valid[:0]
+        else:
+            pick = rng.choice(valid, size=min(len(valid), K // 2 if kind == 3 else K), replace=False)
+            if kind == 3:
+                pick = np.sort(pick)
+        if kind == 3:
+            sel[t, 1:2 * len(pick):2] = pick                 # holes at every even slot
+        else:
+            sel[t, :len(pick)] = pick
+    return sel
+
+
+def test_attention_block_parities():
+    """The float32-output attention (even block ids, then odd ones, the state carried between
+    them) and the single-pass bfloat16-output attention against the oracle on selections that
+    put every block in one pass, in none, or leave holes."""
+    w = W.WORKLOADS["prefill_n4096"].with_(name="parities", seq_len=1800, n_q_heads=8, top_k=8, seed=47)
+    q, k, v = W.prefill_inputs(w, bits=True)
+    sel = _parity_selection(w.seq_len, w.top_k, seed=48)
+    qd, kd, vd = H.to_device(q, w), H.to_device(k, w), H.to_device(v, w)
+    seld = torch.from_numpy(sel[None, None]).to(H.DEV)
+    o, lse = binding.sparse_attn_fwd(qd, kd, vd, seld, return_lse=True, out_dtype=torch.float32)
+    o16 = binding.sparse_attn_fwd(qd, kd, vd, seld)
+    torch.cuda.synchronize()
+    o, lse, o16 = o.cpu().numpy()[0], lse.cpu().numpy()[0], o16.float().cpu().numpy()[0]
+    ts = np.arange(w.seq_len)
+    want, want_lse, _ = oracle.attention(H.host_values(q[0]).astype(np.float64),
+                                         H.host_values(k[0, :, 0]).astype(np.float64),
+                                         H.host_values(v[0, :, 0]).astype(np.float64), sel, ts)
+    empty = np.all(sel < 0, axis=1)
+    assert empty.sum() > 0 and np.all(o[empty] == 0.0) and np.all(o16[empty] == 0.0)
+    assert np.all(np.isneginf(lse[:, empty]))
+    ma, rl = H.attn_errors(o[~empty], want[~empty])
+    assert ma <= 1e-2 and rl <= 5e-3, (ma, rl)
+    H.assert_bf16_output(o16[~empty], want[~empty], "parities bf16")
+    np.testing.assert_allclose(lse[:, ~empty].T, want_lse[~empty], atol=2e-4)
+    H.log(f"[parities] max-abs {ma:.3g} rel-L2 {rl:.3g} over {int((~empty).sum())} rows, {int(empty.sum())} empty")
+
+
 def test_repeat_runs_are_bit_identical():
     w = W.WORKLOADS["prefill_n4096"]
     q, k, v = W.prefill_inputs(w, bits=True)
