@@ -187,8 +187,8 @@ AttnWorkspace attn_layout(const pisa_cfg* c) {
 
 // Passes of a bf16-input attention call: the blocks are split into even and odd ids when the
 // output is float32 (the output rows carry the state between them).  Each pass's gathers then
-// touch half of the blocks, so more of their reads hit the L2: at N = 262144 the two passes take
-// 8.4 ms against 9.5 ms for one, at N = 32768 4.6 against 5.7 ms (without the carried state).
+// touch half of the blocks, so more of their reads hit the L2 (0.55 against 0.48 at N = 262144): the
+// call takes 8.6 ms against 9.4 ms in one pass there, and 4.9 against 5.7 ms at N = 32768.
 constexpr int kAttnPasses = 2;
 
 }  // namespace
