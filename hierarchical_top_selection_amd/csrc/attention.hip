@@ -147,9 +147,12 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
-  // float32 output row of this head (also the carried state between passes); the (m, l) pair
-  float* orow = reinterpret_cast<float*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh;
-  float* ml = a.part_ml + (((int64_t)bh * a.n + t) * a.group + col) * 2;
+  // with several passes (float32 output only): this head's output row, which carries o between the
+  // passes, and its (m, l) pair
+  const bool multi = a.n_passes > 1;
+  float* orow = multi ? reinterpret_cast<float*>(a.o) + b * a.o_sb + (int64_t)t * a.o_st + (int64_t)head * a.o_sh
+                      : nullptr;
+  float* ml = multi ? a.part_ml + (((int64_t)bh * a.n + t) * a.group + col) * 2 : nullptr;
   if (a.pass > 0 && col < a.group) {                   // resume the previous pass's online softmax
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
