@@ -194,7 +194,11 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  *             must satisfy 64 * j <= t (a block with no key <= t contributes
  *             nothing; a token with no such block gets a zero row)
  *   o       : [B][N][H_q][d] output of element type o_dtype (float32 keeps the
- *             fp32 accumulator; bfloat16 rounds it to nearest-even)
+ *             fp32 accumulator; bfloat16 rounds it to nearest-even).  With bf16
+ *             inputs and a float32 output the call runs two passes, even then odd
+ *             block ids, and the rows of o hold the first pass's unnormalised sums
+ *             until the second pass writes the final values; o must not alias q,
+ *             k, v or sel
  *   row_lse : optional float32 [B][H_q][N] output (NULL to skip): natural-log
  *             normaliser of each row's softmax
  *   ws      : workspace of >= pisa_attn_workspace_bytes(cfg) bytes (may be NULL
