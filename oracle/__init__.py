@@ -44,7 +44,11 @@ expansion), flat equivalence when every level keeps all candidates (brute
 force), K >= number of leaves (textbook dense causal attention), attention
 weights summing to one, selection-set invariants (size formula, causal
 validity, lower-index tie rule), decode (incremental update == rebuild,
-decode step == prefill of the last token).
+decode step == prefill of the last token), and the boundary record that the
+acceptance rule reads (K-th minus (K+1)-th score, smallest over the scored
+levels): hand-derived values in tests/golden/route_tiny.json whose minimum
+sits at the top, middle and leaf level, plus agreement with the per-query
+routine's own record on random tiny inputs.
 The general hierarchical case (K smaller than half the leaves) has no worked
 example on the pages: it is pinned only by agreement of the two
 independently written routines plus the invariants above ("parity

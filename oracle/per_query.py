@@ -96,17 +96,28 @@ def score(pyr: Pyramid, heads, level, i, t, scale, mode="lse"):
     return math.fsum(_reduce([dot(q, pyr.vector(level - 1, c)) * scale for c in kids], mode) for q in heads)
 
 
-def select(keys, heads, t, K, C=64, g=2, scale=None, pyr=None, mode="lse"):
-    """Leaf block ids chosen for query position t (sorted ascending)."""
+def select(keys, heads, t, K, C=64, g=2, scale=None, pyr=None, mode="lse", with_gap=False):
+    """Leaf block ids chosen for query position t (sorted ascending).
+
+    With ``with_gap`` also returns the boundary margin of the acceptance rule:
+    at every level holding more than K candidates, the K-th largest score
+    minus the (K+1)-th, and the smallest of these over the levels (inf when no
+    level was scored).
+    """
     pyr = pyr or Pyramid(keys, C, g)
     scale = 1.0 / math.sqrt(len(heads[0])) if scale is None else scale
     level = pyr.top
     cand = [0]
+    margins = []
     while True:
         if len(cand) > K:
-            ranked = sorted(cand, key=lambda i: (-score(pyr, heads, level, i, t, scale, mode), i))
+            scored = {i: score(pyr, heads, level, i, t, scale, mode) for i in cand}
+            ranked = sorted(cand, key=lambda i: (-scored[i], i))
+            margins.append(scored[ranked[K - 1]] - scored[ranked[K]])
             cand = ranked[:K]
         if level == 1:
+            if with_gap:
+                return sorted(cand), min(margins, default=math.inf)
             return sorted(cand)
         nxt = []
         for i in cand:

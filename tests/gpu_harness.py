@@ -4,8 +4,9 @@ sampled tokens, and the comparison rules.
 Comparison rules (from the acceptance criteria of the hot path):
   * selections are compared as sets per (b, kvh, token); a difference is
     allowed only where the oracle's K-th vs (K+1)-th score gap at some scored
-    level is below 1e-3, and such cases must stay under 0.1% of the compared
-    queries (one is tolerated in samples of fewer than 1000 queries);
+    level is below 1e-3, and such cases must stay under 0.1% of the queries a
+    test compares, pooled over all its (b, kvh) units (so a test that compares
+    fewer than 1000 queries allows none);
   * attention is compared against the oracle's attention over the ORACLE's
     selection, which is fed to the GPU kernel as its input: max-abs <= 1e-2 and
     relative L2 <= 5e-3 for bf16 inputs with fp32 accumulation (1e-4 / 1e-5 for
@@ -90,7 +91,8 @@ def compare_selection(gpu_sel: np.ndarray, ora_sel: np.ndarray, gap: np.ndarray,
 
 
 def assert_mismatch_budget(n_bad: int, n_total: int, label: str) -> None:
-    allowed = max(1, int(0.001 * n_total)) if n_total < 1000 else int(0.001 * n_total)
+    """Boundary mismatches pooled over every query one test compares must stay under 0.1%."""
+    allowed = int(0.001 * n_total)
     log(f"{label}: {n_bad} boundary mismatches of {n_total} queries (allowed {allowed})")
     assert n_bad <= allowed, f"{label}: {n_bad} boundary mismatches of {n_total} queries"
 

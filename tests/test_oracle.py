@@ -122,12 +122,56 @@ def test_route_golden_hand_examples():
     with open(os.path.join(GOLDEN, "route_tiny.json")) as f:
         fx = json.load(f)
     for case in fx["cases"]:
+        K = case.get("K", 1)
         k = np.array(case["keys"], dtype=float)[:, None]
         pyr = pisa.build_pyramid(k, C=1, g=2)
-        sel, _ = pisa.route(np.ones((1, 1, 1)), k, pyr, np.array([case["t"]]), K=1, C=1, g=2, scale=1.0)
-        assert list(sel[0]) == case["expected"], case
+        sel, _ = pisa.route(np.ones((1, 1, 1)), k, pyr, np.array([case["t"]]), K=K, C=1, g=2, scale=1.0)
+        assert [int(x) for x in sel[0] if x >= 0] == case["expected"], case
         heads = [[1.0]]
-        assert per_query.select([[x] for x in case["keys"]], heads, case["t"], 1, C=1, g=2, scale=1.0) == case["expected"]
+        assert per_query.select([[x] for x in case["keys"]], heads, case["t"], K, C=1, g=2, scale=1.0) == case["expected"]
+
+
+def test_route_boundary_gap_golden():
+    """The acceptance rule's boundary record (K-th minus (K+1)-th score, smallest over the scored
+    levels) against hand-derived values: cases where the minimum sits at an upper level, at the
+    leaf level and at a middle level, and where the neighbouring differences of the sorted scores
+    (an off-by-one in the positions) or the largest level margin would give another number."""
+    with open(os.path.join(GOLDEN, "route_tiny.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        K = case.get("K", 1)
+        assert case["gap"] == min(case["level_gaps"])
+        k = np.array(case["keys"], dtype=float)[:, None]
+        pyr = pisa.build_pyramid(k, C=1, g=2)
+        _, gap = pisa.route(np.ones((1, 1, 1)), k, pyr, np.array([case["t"]]), K=K, C=1, g=2, scale=1.0)
+        assert abs(gap[0] - case["gap"]) <= 1e-6, (case["keys"], case["t"], gap[0], case["gap"])
+        sel, pq_gap = per_query.select([[x] for x in case["keys"]], [[1.0]], case["t"], K, C=1, g=2, scale=1.0,
+                                       with_gap=True)
+        assert sel == case["expected"] and abs(pq_gap - case["gap"]) <= 1e-6, (case["keys"], pq_gap)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_gap_agrees_with_independent_per_query_routine(seed):
+    """The boundary record of the level-wise oracle equals the independently written per-query
+    routine's (its own pyramid, LSE and sort) on random tiny inputs, ties included."""
+    rng = np.random.default_rng(300 + seed)
+    C, G, K, n = [(2, 2, 2, 60), (4, 1, 3, 100), (4, 3, 2, 90), (2, 2, 4, 70)][seed]
+    k = np.round(rng.standard_normal((n, 4)) * 2) / 2         # coarse values: some exact ties
+    q = np.round(rng.standard_normal((n, G, 4)) * 2) / 2 + 0.5
+    pyr = pisa.build_pyramid(k, C, 2)
+    sel, gap = pisa.route(q, k, pyr, np.arange(n), K, C, 2)
+    ref_pyr = per_query.Pyramid(k.tolist(), C, 2)
+    n_zero = n_inf = 0
+    for t in range(n):
+        want, want_gap = per_query.select(k.tolist(), q[t].tolist(), t, K, C, 2, pyr=ref_pyr, with_gap=True)
+        assert [int(x) for x in sel[t] if x >= 0] == want, t
+        if math.isinf(want_gap):
+            assert math.isinf(gap[t]), (t, gap[t])
+            n_inf += 1
+        else:
+            assert abs(gap[t] - want_gap) <= 1e-9 * max(1.0, abs(want_gap)), (t, gap[t], want_gap)
+            n_zero += want_gap == 0.0
+    assert n_inf > 0 and n_inf < n                             # early tokens score no level
 
 
 @pytest.mark.parametrize("C,G,n", [(4, 1, 40), (4, 2, 64), (8, 4, 72), (2, 3, 33)])
