@@ -120,6 +120,32 @@ def _tensor(t: torch.Tensor, token_axis: bool = True) -> PisaTensor:
     return PisaTensor(t.data_ptr(), sb, st, sh)
 
 
+def _extent(t: torch.Tensor) -> tuple[int, int]:
+    """Byte range [start, end) that a (possibly strided) tensor's elements span."""
+    if t.numel() == 0:
+        return t.data_ptr(), t.data_ptr()
+    last = sum((size - 1) * stride for size, stride in zip(t.shape, t.stride()))
+    return t.data_ptr(), t.data_ptr() + (last + 1) * t.element_size()
+
+
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    (a0, a1), (b0, b1) = _extent(a), _extent(b)
+    return a0 < b1 and b0 < a1
+
+
+def _expect(name: str, t: torch.Tensor, shape, dtype=None, device=None) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ws_bytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -174,18 +200,23 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, pyr: torch.Tensor, top_k: in
     """
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
+    _expect("k", k, (B, N, Hkv, d), q.dtype, q.device)
+    _expect("pyramid", pyr, (B, Hkv, pyramid_nodes(N), d), torch.float32, q.device)
     cfg = _cfg_from(q, k, top_k, scale)
     cfg.score = SCORES[score]
     need = select_workspace_bytes(cfg)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _ws_bytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, Hkv, N, top_k), dtype=torch.int32, device=q.device)
+    _expect("out", out, (B, Hkv, N, top_k), torch.int32, q.device)
+    if not out.is_contiguous() or not pyr.is_contiguous():
+        raise ValueError("the selection and the pyramid must be contiguous")
     scores = torch.empty((B, Hkv, N, top_k), dtype=torch.float32, device=q.device) if return_scores else None
     _check("pisa_select_blocks", lib().pisa_select_blocks(
         ctypes.byref(cfg), _tensor(q), _tensor(k), ctypes.c_void_p(pyr.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(scores.data_ptr() if scores is not None else 0),
-        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(_ws_bytes(workspace)), _stream(q)))
     return (out, scores) if return_scores else out
 
 
@@ -198,17 +229,22 @@ def select_flat(q: torch.Tensor, pyr: torch.Tensor, n_kv_heads: int, top_k: int,
                 return_scores: bool = False):
     """Single-level (flat) top-K leaf selection by mean-key scores: int32 [B, Hkv, N, K] (and scores)."""
     B, N, Hq, d = q.shape
+    _dtype_code(q)
+    _expect("pyramid", pyr, (B, n_kv_heads, pyramid_nodes(N), d), torch.float32, q.device)
     cfg = make_cfg(B, N, Hq, n_kv_heads, d, top_k, q.dtype, scale)
     need = flat_workspace_bytes(cfg)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _ws_bytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, n_kv_heads, N, top_k), dtype=torch.int32, device=q.device)
+    _expect("out", out, (B, n_kv_heads, N, top_k), torch.int32, q.device)
+    if not out.is_contiguous() or not pyr.is_contiguous():
+        raise ValueError("the selection and the pyramid must be contiguous")
     scores = torch.empty((B, n_kv_heads, N, top_k), dtype=torch.float32, device=q.device) if return_scores else None
     _check("pisa_select_flat", lib().pisa_select_flat(
         ctypes.byref(cfg), _tensor(q), ctypes.c_void_p(pyr.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(scores.data_ptr() if scores is not None else 0),
-        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(_ws_bytes(workspace)), _stream(q)))
     return (out, scores) if return_scores else out
 
 
@@ -225,16 +261,23 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
     """
     B, N, Hq, d = q.shape
     top_k = sel.shape[-1]
+    Hkv = k.shape[2]
+    _expect("k", k, (B, N, Hkv, d), q.dtype, q.device)
+    _expect("v", v, (B, N, Hkv, d), q.dtype, q.device)
     cfg = _cfg_from(q, k, top_k, scale)
-    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, k.shape[2], N, top_k):
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, Hkv, N, top_k):
         raise ValueError("selection must be a contiguous int32 [B, Hkv, N, K] tensor")
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _expect("out", out, q.shape, out_dtype, q.device)
+    _dtype_code(out)
+    if any(_overlap(out, x) for x in (q, k, v, sel)):
+        raise ValueError("out must not overlap q, k, v or the selection")
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
     need = attn_workspace_bytes(cfg)
-    if need and (workspace is None or workspace.numel() < need):
+    if need and (workspace is None or _ws_bytes(workspace) < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if need else (0, 0)
+    ws_ptr, ws_len = (workspace.data_ptr(), _ws_bytes(workspace)) if need else (0, 0)
     _check("pisa_sparse_attn_fwd", lib().pisa_sparse_attn_fwd(
         ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()),
         _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
@@ -261,22 +304,23 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
         raise ValueError("o and dout must have q's shape and one dtype")
     if row_lse.dtype != torch.float32 or not row_lse.is_contiguous() or row_lse.shape != (B, Hq, N):
         raise ValueError("row_lse must be a contiguous float32 [B, Hq, N] tensor")
+    _expect("k", k, (B, N, k.shape[2], d), q.dtype, q.device)
+    _expect("v", v, k.shape, q.dtype, q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(q.shape, **f32) if dq is None else dq
     dk = torch.empty(k.shape, **f32) if dk is None else dk
     dv = torch.empty(v.shape, **f32) if dv is None else dv
-    for x in (dq, dk, dv):
-        if x.dtype != torch.float32:
-            raise ValueError("gradients are float32")
+    for name, x, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _expect(name, x, ref.shape, torch.float32, q.device)
     need = attn_bwd_workspace_bytes(cfg)
     if need == 0:
         raise RuntimeError("pisa_sparse_attn_bwd: unsupported configuration")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _ws_bytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("pisa_sparse_attn_bwd", lib().pisa_sparse_attn_bwd(
         ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()), _tensor(o),
         _tensor(dout), _dtype_code(dout), ctypes.c_void_p(row_lse.data_ptr()), _tensor(dq), _tensor(dk), _tensor(dv),
-        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), _stream(q)))
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(_ws_bytes(workspace)), _stream(q)))
     return dq, dk, dv
 
 
@@ -290,12 +334,25 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cac
     """
     B, cap, Hkv, d = k_cache.shape
     Hq = q.shape[1]
-    cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, k_cache.dtype, scale, score)
+    dt, dev = k_cache.dtype, k_cache.device
     _dtype_code(k_cache)
+    _expect("q", q, (B, Hq, d), dt, dev)
+    _expect("k_new", k_new, (B, Hkv, d), dt, dev)
+    _expect("v_new", v_new, (B, Hkv, d), dt, dev)
+    _expect("v_cache", v_cache, k_cache.shape, dt, dev)
+    _expect("pyramid", pyr, (B, Hkv, pyramid_nodes(cap), d), torch.float32, dev)
+    if not pyr.is_contiguous():
+        raise ValueError("the pyramid must be contiguous")
+    cfg = make_cfg(B, cap, Hq, Hkv, d, top_k, dt, scale, score)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _expect("out", out, q.shape, out_dtype, dev)
+    _dtype_code(out)
     if sel_out is None:
         sel_out = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
+    _expect("sel_out", sel_out, (B, Hkv, top_k), torch.int32, dev)
+    if not sel_out.is_contiguous():
+        raise ValueError("sel_out must be contiguous")
     _check("pisa_decode_step", lib().pisa_decode_step(
         ctypes.byref(cfg), n_ctx, _tensor(q, False), _tensor(k_new, False), _tensor(v_new, False),
         _tensor(k_cache), _tensor(v_cache), ctypes.c_void_p(pyr.data_ptr()), ctypes.c_void_p(sel_out.data_ptr()),

@@ -120,8 +120,13 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   const bf16x8* kpack = a.kpack + (int64_t)bh * m1 * (kLeaf * D / 8);
   const bf16x8* vpack = a.vpack + (int64_t)bh * m1 * (kLeaf * D / 8);
   const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
-  // entries < 0 are skipped; with several passes this one takes the blocks j % n_passes == pass
-  const uint64_t valid = __ballot(my_sel >= 0 && (a.n_passes == 1 || my_sel % a.n_passes == a.pass));
+  // The key set is the union of the listed blocks cut to positions <= t: an entry takes part if
+  // 0 <= j <= t / 64 (so j < ceil(n / 64) and every gather below stays inside the packed blocks)
+  // and no lower slot of the row lists the same id.  With several passes this one takes the
+  // blocks j % n_passes == pass.
+  bool use = my_sel >= 0 && my_sel <= t / kLeaf;
+  for (int i = 0; i < a.top_k; ++i) use = use && !(i < lane && __builtin_amdgcn_readlane(my_sel, i) == my_sel);
+  const uint64_t valid = __ballot(use && (a.n_passes == 1 || my_sel % a.n_passes == a.pass));
   const int nsel = __popcll(valid);
   const float c2 = a.scale * kLog2e;
 
@@ -276,7 +281,11 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
 
   for (int s = 0; s < a.top_k; ++s) {
     const int j = sel[s];
-    if (j < 0) continue;
+    // union of the listed blocks cut to positions <= t: skip -1, blocks past t and repeats
+    if (j < 0 || j > t / kLeaf) continue;
+    bool repeat = false;
+    for (int s2 = 0; s2 < s; ++s2) repeat = repeat || sel[s2] == j;
+    if (repeat) continue;
     const int64_t first = (int64_t)j * kLeaf;
     floatx4 acc[4];
 #pragma unroll

@@ -190,9 +190,11 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  * attention; Method steps, fourth step): the key set of token t is the union
  * of blocks in sel[b][kvh][t] cut to positions <= t; fp32 accumulation.
  *   q, k, v : cfg->dtype, shapes as in select_blocks (v like k)
- *   sel     : int32 [B][H_kv][N][K]; entries < 0 are skipped; valid entries
- *             must satisfy 64 * j <= t (a block with no key <= t contributes
- *             nothing; a token with no such block gets a zero row)
+ *   sel     : int32 [B][H_kv][N][K]; the key set of token t is the union of
+ *             the listed blocks j with 0 <= j <= t / 64: entries < 0, entries
+ *             past t / 64 and repeats of an id listed earlier in the row are
+ *             skipped, so any int32 content is memory-safe (a token with no
+ *             such block gets a zero row and row LSE -inf)
  *   o       : [B][N][H_q][d] output of element type o_dtype (float32 keeps the
  *             fp32 accumulator; bfloat16 rounds it to nearest-even).  With bf16
  *             inputs and a float32 output the call runs two passes, even then odd

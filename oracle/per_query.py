@@ -141,9 +141,10 @@ def flat_select(keys, heads, t, K, C=64, scale=None):
 
 
 def attend(keys, values, heads, blocks, t, C=64, scale=None):
-    """Softmax attention of each head over the keys of ``blocks`` at positions <= t."""
+    """Softmax attention of each head over the keys of ``blocks`` at positions <= t (a block
+    listed twice counts once)."""
     scale = 1.0 / math.sqrt(len(heads[0])) if scale is None else scale
-    pos = [r for j in blocks for r in range(j * C, min((j + 1) * C, len(keys))) if r <= t]
+    pos = [r for j in sorted(set(blocks)) if j >= 0 for r in range(j * C, min((j + 1) * C, len(keys))) if r <= t]
     out = []
     for q in heads:
         logits = [dot(q, keys[r]) * scale for r in pos]

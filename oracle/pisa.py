@@ -332,12 +332,22 @@ def leaf_lse(q: np.ndarray, k: np.ndarray, j: int, t: int, C: int = 64,
 
 
 # ----------------------------------------------------------------------------- attention
+def union_rows(sel: np.ndarray) -> np.ndarray:
+    """Each row's listed block ids as a set (R5): repeats become -1 (int64, same shape)."""
+    srt = np.sort(np.asarray(sel, dtype=np.int64), axis=1)
+    repeat = np.zeros(srt.shape, dtype=bool)
+    repeat[:, 1:] = srt[:, 1:] == srt[:, :-1]
+    return np.where(repeat, -1, srt)
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, ts: np.ndarray,
               C: int = 64, scale: float | None = None):
     """Softmax attention of each token's group heads over its selected blocks [Prereq/BSA; Steps: fourth step].
 
     Keys are the union of blocks j in I_t, positions [jC, min((j+1)C, n))
-    cut to <= t (R5).  Returns (o [T, G, d], lse [T, G], weight sums [T, G]).
+    cut to <= t (R5): a block listed twice contributes its keys once, and
+    entries < 0 or past t contribute none.  Returns (o [T, G, d], lse [T, G],
+    weight sums [T, G]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -346,9 +356,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, ts: 
     T, G, d = q.shape
     n = k.shape[0]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
+    sel = union_rows(sel)
     Ks = sel.shape[1]
-    pos = np.asarray(sel, dtype=np.int64)[:, :, None] * C + np.arange(C)[None, None, :]
-    ok = (np.asarray(sel)[:, :, None] >= 0) & (pos < n) & (pos <= ts[:, None, None])
+    pos = sel[:, :, None] * C + np.arange(C)[None, None, :]
+    ok = (sel[:, :, None] >= 0) & (pos < n) & (pos <= ts[:, None, None])
     pos = np.where(ok, pos, 0).reshape(T, Ks * C)
     ok = ok.reshape(T, Ks * C)
     logits = np.matmul(q, np.transpose(k[pos], (0, 2, 1))) * scale                 # [T, G, Ks*C]
@@ -383,7 +394,7 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndar
     dv = np.zeros_like(v)
     for r in range(T):
         t = int(ts[r])
-        blocks = [int(j) for j in sel[r] if j >= 0]
+        blocks = sorted({int(j) for j in sel[r] if j >= 0})         # the union of the listed blocks (R5)
         pos = np.array([p for j in blocks for p in range(j * C, min((j + 1) * C, n)) if p <= t], dtype=np.int64)
         if pos.size == 0:
             continue

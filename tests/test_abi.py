@@ -138,3 +138,42 @@ def test_backward_validation_and_workspace(lib):
     assert call(gd=5) == 1                                    # gradient type
     assert call(q=bad) == 1 and call(dq=bad) == 1             # misaligned tensors
     assert call(lse_ptr=None) == 1                            # row LSE required
+
+
+def test_binding_rejects_mismatched_tensors_before_any_call():
+    """The Python binding checks dtype and shape agreement, output overlap and workspace size in
+    bytes before it reaches the library (CPU tensors: nothing is launched)."""
+    import torch
+
+    B, N, Hq, Hkv, d, K = 1, 256, 4, 1, 64, 2
+    q = torch.zeros((B, N, Hq, d), dtype=torch.bfloat16)
+    k = torch.zeros((B, N, Hkv, d), dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    sel = torch.zeros((B, Hkv, N, K), dtype=torch.int32)
+    with pytest.raises(ValueError, match="dtype"):            # a float32 q with bfloat16 K/V
+        binding.sparse_attn_fwd(q.float(), k, v, sel)
+    with pytest.raises(ValueError, match="shape"):            # v of another length
+        binding.sparse_attn_fwd(q, k, v[:, :128], sel)
+    with pytest.raises(ValueError, match="shape"):            # undersized output
+        binding.sparse_attn_fwd(q, k, v, sel, out=torch.empty((B, N - 1, Hq, d), dtype=torch.float32))
+    with pytest.raises(ValueError, match="overlap"):          # output aliasing q
+        binding.sparse_attn_fwd(q, k, v, sel, out=q)
+    packed = torch.zeros((B, N, Hq + 2 * Hkv, d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="overlap"):          # output aliasing a view of a packed QKV buffer
+        binding.sparse_attn_fwd(packed[:, :, :Hq], packed[:, :, Hq:Hq + 1], packed[:, :, Hq + 1:], sel,
+                                out=packed[:, :, :Hq])
+    assert not binding._overlap(packed[:, :, :Hq], q)
+    pyr = torch.zeros((B, Hkv, binding.pyramid_nodes(N), d), dtype=torch.float32)
+    with pytest.raises(ValueError, match="shape"):            # pyramid of another capacity
+        binding.select_blocks(q, k, pyr[:, :, 1:], K)
+    with pytest.raises(ValueError, match="dtype"):
+        binding.select_blocks(q, k.float(), pyr, K)
+    kc = torch.zeros((2, 300, Hkv, d), dtype=torch.bfloat16)
+    dpyr = torch.zeros((2, Hkv, binding.pyramid_nodes(300), d), dtype=torch.float32)
+    qn = torch.zeros((2, Hq, d), dtype=torch.bfloat16)
+    kn = torch.zeros((2, Hkv, d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dtype"):            # float32 query against bfloat16 caches
+        binding.decode_step(qn.float(), kn, kn, kc, kc.clone(), dpyr, 10, K)
+    with pytest.raises(ValueError, match="shape"):            # pyramid sized for another capacity
+        binding.decode_step(qn, kn, kn, kc, kc.clone(), dpyr[:, :, :-1], 10, K)
+    assert binding._ws_bytes(torch.empty(10, dtype=torch.float32)) == 40

@@ -204,6 +204,41 @@ def test_attention_block_parities():
     H.log(f"[parities] max-abs {ma:.3g} rel-L2 {rl:.3g} over {int((~empty).sum())} rows, {int(empty.sum())} empty")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_ignores_negative_future_and_repeated_ids(dtype):
+    """Selection rows with -1, repeated ids, ids past t, past the last block, INT32_MAX and INT32_MIN:
+    every path (two-pass float32 output, one-pass bfloat16 output, float32 inputs) attends over the
+    union of the listed blocks cut to positions <= t, as the oracle does on the same rows."""
+    w = W.WORKLOADS["prefill_n4096"].with_(name="bad_ids", seq_len=1300, n_q_heads=8, top_k=12, seed=49,
+                                           dtype=dtype)
+    N, K = w.seq_len, w.top_k
+    m1 = -(-N // 64)
+    rng = np.random.default_rng(50)
+    sel = np.full((N, K), -1, dtype=np.int64)
+    for t in range(N):
+        valid = np.arange(t // 64 + 1)
+        pick = list(rng.choice(valid, size=min(len(valid), 4), replace=False))
+        row = pick + pick[:2] + [t // 64 + 1, m1, m1 + 7, 2 ** 31 - 1, -2 ** 31, -1]
+        sel[t, :len(row)] = rng.permutation(row)[:K]
+    q, k, v = W.prefill_inputs(w, bits=True)
+    qd, kd, vd = H.to_device(q, w), H.to_device(k, w), H.to_device(v, w)
+    seld = torch.from_numpy(sel.astype(np.int32)[None, None]).to(H.DEV)
+    H.log(f"[bad_ids {dtype}] GPU attention")
+    o, lse = binding.sparse_attn_fwd(qd, kd, vd, seld, return_lse=True, out_dtype=torch.float32)
+    o_native = binding.sparse_attn_fwd(qd, kd, vd, seld)
+    torch.cuda.synchronize()
+    want, want_lse, _ = oracle.attention(H.host_values(q[0]).astype(np.float64),
+                                         H.host_values(k[0, :, 0]).astype(np.float64),
+                                         H.host_values(v[0, :, 0]).astype(np.float64), sel, np.arange(N))
+    tol_abs, tol_rel = H.attn_tolerance(w)
+    ma, rl = H.attn_errors(o.cpu().numpy()[0], want)
+    assert ma <= tol_abs and rl <= tol_rel, (dtype, ma, rl)
+    np.testing.assert_allclose(lse.cpu().numpy()[0].T, want_lse, atol=2e-4 if dtype == "bf16" else 2e-5)
+    if dtype == "bf16":
+        H.assert_bf16_output(o_native.float().cpu().numpy()[0], want, "bad_ids bf16 output")
+    H.log(f"[bad_ids {dtype}] max-abs {ma:.3g} rel-L2 {rl:.3g}")
+
+
 def test_repeat_runs_are_bit_identical():
     w = W.WORKLOADS["prefill_n4096"]
     q, k, v = W.prefill_inputs(w, bits=True)

@@ -297,6 +297,49 @@ def test_attention_matches_per_query_routine():
         np.testing.assert_allclose(o[r], want, atol=1e-13)
 
 
+def _messy_rows(n, C, K, rng):
+    """Rows listing every block j <= t / C (some twice, in random order) plus ids past t, -1 and
+    ids beyond the last block."""
+    m1 = -(-n // C)
+    sel = np.full((n, K), -1, dtype=np.int64)
+    for t in range(n):
+        ids = list(range(t // C + 1))
+        ids += list(rng.choice(ids, size=min(2, len(ids)), replace=False))          # repeats
+        ids += [t // C + 1, m1 + 3, 10 ** 6, -1]                                     # past t / absent
+        ids = list(rng.permutation(ids))
+        sel[t, :len(ids)] = ids
+    return sel
+
+
+def test_attention_union_reading_reduces_to_dense_causal_attention():
+    """Reading R5: the key set is the union of the listed blocks cut to <= t.  Rows that list every
+    valid block, some of them twice and in random order, plus ids past t or past the last block,
+    give textbook dense causal attention; the gradients equal float64 autograd of it."""
+    import torch
+
+    rng = np.random.default_rng(23)
+    C, n, G, d = 8, 45, 2, 4
+    k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    q = rng.standard_normal((n, G, d))
+    do = rng.standard_normal((n, G, d))
+    ts = np.arange(n)
+    sel = _messy_rows(n, C, 16, rng)
+    o, lse, wsum = pisa.attention(q, k, v, sel, ts, C)
+    np.testing.assert_allclose(o, pisa.dense_causal_attention(q, k, v, ts), atol=1e-12)
+    np.testing.assert_allclose(wsum, 1.0, atol=1e-13)
+    for t in (0, 17, 44):                                        # the independent routine, same rows
+        want = per_query.attend(k.tolist(), v.tolist(), q[t].tolist(), [int(x) for x in sel[t]], t, C)
+        np.testing.assert_allclose(o[t], want, atol=1e-13)
+    dq, dk, dv = pisa.attention_backward(q, k, v, sel, ts, do, C=C)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    logits = torch.einsum("tgd,sd->tgs", qt, kt) / math.sqrt(d)
+    mask = torch.arange(n)[None, :] > torch.arange(n)[:, None]
+    out = torch.einsum("tgs,sd->tgd", torch.softmax(logits.masked_fill(mask[:, None, :], float("-inf")), -1), vt)
+    out.backward(torch.tensor(do))
+    for got, want in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- decode
 def test_decode_step_equals_prefill_of_last_token():
     """Method steps, third step: decode at length n+1 equals prefill's result for token n."""
