@@ -80,7 +80,8 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
         pool.terminate()
     units = w.batch * w.n_kv_heads
     full_s = units * t_pyr + units * w.seq_len * elapsed / done
-    return {"value": w.batch * w.seq_len / full_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+    return {"value": w.batch * w.seq_len / full_s, "unit": "tokens/s", "cores": workers,
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{done} query tokens of (b=0, kvh=0) drawn uniformly from the {w.seq_len}-token sequence "
                       f"(fp64 NumPy routing, leaf LSE, top-K and attention) in {elapsed:.1f} s on {workers} "
                       f"processes, plus one pyramid build ({t_pyr:.2f} s); extrapolated to "
@@ -116,7 +117,78 @@ def attention_flops(sel, n: int, group: int, d: int) -> float:
     return float(valid.sum().item()) * group * 4.0 * d
 
 
+def level_sizes(n: int) -> list[int]:
+    """Nodes per pyramid level for n keys, leaves first: ceil(n / 64), then ceil(/2) down to 1."""
+    sizes = [-(-n // 64)]
+    while sizes[-1] > 1:
+        sizes.append(-(-sizes[-1] // 2))
+    return sizes
+
+
+def compulsory_bytes(w: W.Workload) -> dict:
+    """HBM bytes each prefill kernel must move at the least: every input it reads once, every
+    output it writes once (per launch; the attention kernel's per call)."""
+    B, N, G, d, K = w.batch, w.seq_len, w.group, w.head_dim, w.top_k
+    bh, s, width = w.batch * w.n_kv_heads, (2 if w.dtype == "bf16" else 4), 2 * K
+    sizes = level_sizes(N)
+    m1, nodes = sizes[0], sum(sizes)
+    windows = -(-N // (512 if N <= 65536 else 1024))
+    slots = bh * N * width * 4
+    q_bytes = bh * N * G * d * s
+    packed = bh * m1 * 64 * d * 2
+    return {
+        "pyramid_leaves_kernel": bh * N * d * s + bh * sum(sizes[:4]) * d * 4,
+        "pyramid_top_kernel": bh * (sizes[3] if len(sizes) > 3 else 0) * d * 4 + bh * sum(sizes[4:]) * d * 4,
+        "split_summaries_kernel": bh * nodes * d * 4 + bh * sum(-(-m // 2) for m in sizes) * 8 * d,
+        "route_kernel": q_bytes + (bh * N * G * d * 2 if w.dtype == "bf16" else 0) + slots,
+        "cluster_kernel": 2 * slots + bh * windows * (m1 + 1) * 4,
+        "pack_blocks_kernel": bh * N * d * 2 + packed,
+        "leaf_lse_kernel": bh * N * G * d * 2 + packed + 2 * slots,
+        "topk_kernel": 2 * slots + bh * N * K * 4,
+        "attention_pack": 2 * (bh * N * d * 2 + packed),
+    }
+
+
+def decode_step_bytes(w: W.Workload, n_ctx: int) -> int:
+    """HBM bytes one decode step must move at the least, for every (b, kvh) unit, with the new token
+    at position n_ctx (all nodes valid): the children summaries of every scored level, the raw keys of
+    the candidate leaves, the values of the K selected blocks, the queries and outputs, the appended
+    key and value, and the refreshed leaf with its ancestor path.  Candidate counts take the upper
+    bound min(2 * kept, level size) at every level."""
+    d, G, K, s = w.head_dim, w.group, w.top_k, (2 if w.dtype == "bf16" else 4)
+    sizes = level_sizes(n_ctx + 1)
+    per = 0
+    cand = 1                                            # the root
+    for lvl in range(len(sizes), 1, -1):                # children live at level lvl - 1
+        kids = min(2 * min(cand, K), sizes[lvl - 2])
+        if cand > K:
+            per += min(2 * cand, sizes[lvl - 2]) * d * 4  # children summaries of every candidate
+        cand = kids
+    per += cand * 64 * d * s                            # raw keys of the candidate leaves
+    per += min(K, sizes[0]) * 64 * d * s                # values of the selected blocks
+    per += G * d * s + G * d * s                        # query rows in, output rows out
+    per += 2 * d * s * 2                                # new key and value, read and written
+    per += 64 * d * s + 2 * len(sizes) * d * 4          # the leaf's keys, ancestor path read and written
+    return per * w.batch * w.n_kv_heads
+
+
+def stage_kernels(w: W.Workload) -> dict:
+    """Kernels each entry point launches, in launch order, for a prefill workload (their names)."""
+    bf16 = w.dtype == "bf16"
+    levels = len(level_sizes(w.seq_len))
+    return {
+        "pyramid": ["pyramid_leaves_kernel"] + (["pyramid_top_kernel"] if levels > 4 else []),
+        "select": (["split_summaries_kernel"] if bf16 else []) + ["route_kernel", "cluster_kernel"]
+                  + (["pack_blocks_kernel"] if bf16 else []) + ["leaf_lse_kernel", "topk_kernel"],
+        "attention": (["pack_blocks_kernel", "attention_bf16_kernel", "attention_bf16_kernel"] if bf16
+                      else ["attention_f32_kernel"]),
+    }
+
+
 def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
+    """Timed prefill steps.  Besides the host wall clock and the events around each entry point,
+    the library records one event after every kernel it enqueues (pisa_stage_events), so every
+    kernel's duration is measured on the stream it runs on."""
     import torch
 
     from hierarchical_top_selection_amd import binding
@@ -131,35 +203,48 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
     ws_attn = torch.empty(max(1, binding.attn_workspace_bytes(cfg)), dtype=torch.uint8, device=q.device)
     sel = torch.empty((B, w.n_kv_heads, N, K), dtype=torch.int32, device=q.device)
     o = torch.empty(q.shape, dtype=torch.float32, device=q.device)   # fp32 attention output
+    names = stage_kernels(w)
+    calls = ("pyramid", "select", "attention")
 
     def step(ev=None):
+        # ev: per call, [start, one event per kernel]
         if ev is not None:
-            ev[0].record()
+            ev["pyramid"][0].record()
+            binding.stage_events(ev["pyramid"][1:])
         binding.build_pyramid(k, out=pyr)
         if ev is not None:
-            ev[1].record()
+            ev["select"][0].record()
+            binding.stage_events(ev["select"][1:])
         binding.select_blocks(q, k, pyr, K, workspace=ws, out=sel)
         if ev is not None:
-            ev[2].record()
+            ev["attention"][0].record()
+            binding.stage_events(ev["attention"][1:])
         binding.sparse_attn_fwd(q, k, v, sel, out=o, workspace=ws_attn)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    events = [{c: [torch.cuda.Event(enable_timing=True) for _ in range(1 + len(names[c]))] for c in calls}
+              for _ in range(steps)]
+    for ev in events:                      # create the events before the timed region
+        for lst in ev.values():
+            for e in lst:
+                e.record()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    pyr_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
-    sel_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in events) / steps
+    call_ms = {c: sum(ev[c][0].elapsed_time(ev[c][-1]) for ev in events) / steps for c in calls}
+    kernel_ms = {c: [sum(ev[c][i].elapsed_time(ev[c][i + 1]) for ev in events) / steps
+                     for i in range(len(names[c]))] for c in calls}
     flops = attention_flops(sel, N, w.group, d)
-    return {"workload": w, "ms_per_step": wall_ms, "pyramid_ms": pyr_ms, "select_ms": sel_ms,
-            "attn_ms": attn_ms, "tokens_per_s": B * N / (wall_ms / 1e3), "attn_flops": flops}
+    cand = ws[:B * w.n_kv_heads * N * 2 * K * 4].view(torch.int32).view(B, w.n_kv_heads, N, 2 * K)
+    leaf_flops = attention_flops(cand, N, w.group, d) / 2.0          # Q K^T only: 2 d per (head, key)
+    return {"workload": w, "ms_per_step": wall_ms, "pyramid_ms": call_ms["pyramid"], "select_ms": call_ms["select"],
+            "attn_ms": call_ms["attention"], "tokens_per_s": B * N / (wall_ms / 1e3), "attn_flops": flops,
+            "leaf_flops": leaf_flops, "kernel_names": names, "kernel_ms": kernel_ms}
 
 
 def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
@@ -366,29 +451,90 @@ def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
     total_ms = ev[0].elapsed_time(ev[1])
     del kc, vc
     torch.cuda.empty_cache()
-    return {"tokens_per_s": B * S / (total_ms * 1e-3), "ms_per_step": total_ms / S, "steps": S, "batch": B,
-            "context": n0, "data": "synthetic: device-drawn N(0,1), seeded torch generator"}
+    ms = total_ms / S
+    step_bytes = sum(decode_step_bytes(w, n0 + i) for i in range(S)) / S
+    return {"tokens_per_s": B * S / (total_ms * 1e-3), "ms_per_step": ms, "steps": S, "batch": B,
+            "context": n0, "data": "synthetic: device-drawn N(0,1), seeded torch generator",
+            "roofline": {"bound": "hbm", "bytes_per_step": step_bytes, "achieved": step_bytes / (ms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
-# Counter summary of the dominant kernel (committed under profiles/).  Its traffic figure is
-# reported only while the kernel's sources are the ones the counters were taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_n262144_traffic.md")
-TRAFFIC_SOURCES = ("attention.hip", "kernels.h", "pisa_device.h")
+# HBM-side traffic per launch of each kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by
+# a plain device copy (committed under profiles/).  A kernel's figure is reported only while its
+# sources are the ones the counters were taken on; otherwise it is null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_n262144_traffic.md")
+_COMMON = ("kernels.h", "pisa_device.h")
+KERNEL_SOURCES = {
+    "pyramid_leaves_kernel": ("pyramid.hip", "pyramid_dev.h") + _COMMON,
+    "pyramid_top_kernel": ("pyramid.hip", "pyramid_dev.h") + _COMMON,
+    "split_summaries_kernel": ("route.hip",) + _COMMON,
+    "route_kernel": ("route.hip",) + _COMMON,
+    "cluster_kernel": ("cluster.hip",) + _COMMON,
+    "pack_blocks_kernel": ("pack.hip",) + _COMMON,
+    "leaf_lse_kernel": ("leaf_lse.hip",) + _COMMON,
+    "topk_kernel": ("topk.hip",) + _COMMON,
+    "attention_bf16_kernel": ("attention.hip",) + _COMMON,
+}
 
 
-def attention_traffic(workload: str):
-    """HBM-side bytes per attention call, both passes (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
-    if workload != "prefill_n262144" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    fields = dict(re.findall(r"^(source_sha256|fetch_bytes_per_call|write_bytes_per_call): (\S+)\s*$",
-                             open(TRAFFIC_FILE).read(), re.M))
+def source_sha256(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "hierarchical_top_selection_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    if len(fields) != 3 or h.hexdigest() != fields["source_sha256"]:
-        return None
-    return int(fields["fetch_bytes_per_call"]) + int(fields["write_bytes_per_call"])
+    return h.hexdigest()
+
+
+def kernel_traffic(workload: str) -> dict:
+    """{kernel: HBM-side bytes per launch} for the kernels whose committed counters match the current
+    sources (record lines `traffic: <kernel> fetch=<bytes> write=<bytes> sha256=<hex>`)."""
+    if workload != "prefill_n262144" or not os.path.exists(TRAFFIC_FILE):
+        return {}
+    out = {}
+    for name, fetch, write, sha in re.findall(r"^traffic: (\w+) fetch=(\d+) write=(\d+) sha256=([0-9a-f]+)\s*$",
+                                              open(TRAFFIC_FILE).read(), re.M):
+        if name in KERNEL_SOURCES and sha == source_sha256(name):
+            out[name] = int(fetch) + int(write)
+    return out
+
+
+def kernel_table(run: dict) -> list:
+    """Per-kernel duration (HIP events on the launch stream), compulsory HBM bytes and their rate
+    against the 8 TB/s peak, counter traffic where current, and the MFMA rate of the leaf scores."""
+    w = run["workload"]
+    need = compulsory_bytes(w)
+    traffic = kernel_traffic(w.name)
+    rows = []
+    for call in ("pyramid", "select"):
+        for name, ms in zip(run["kernel_names"][call], run["kernel_ms"][call]):
+            row = {"kernel": name, "call": call, "ms": ms, "bytes": need[name],
+                   "achieved_gbs": need[name] / (ms * 1e-3) / 1e9}
+            row["frac"] = row["achieved_gbs"] / HBM_PEAK_GBS
+            tr = traffic.get(name)
+            row["traffic"] = tr
+            row["traffic_frac"] = None if tr is None else tr / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+            if name == "leaf_lse_kernel":
+                peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+                row["flops"] = run["leaf_flops"]
+                row["mfma_frac"] = run["leaf_flops"] / (ms * 1e-3) / 1e12 / peak
+            rows.append(row)
+    return rows
+
+
+def attention_roofline(run: dict) -> dict:
+    """The attention kernel against the bf16 MFMA peak: valid-key flops of one call over the summed
+    durations of its launches (one per pass), each timed with HIP events on the launch stream."""
+    w = run["workload"]
+    names, ms = run["kernel_names"]["attention"], run["kernel_ms"]["attention"]
+    kernel = names[-1]
+    launch_ms = [m for n, m in zip(names, ms) if n == kernel]
+    tflops = run["attn_flops"] / (sum(launch_ms) * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    traffic = kernel_traffic(w.name).get(kernel)
+    return {"kernel": kernel, "launches": len(launch_ms), "launch_ms": launch_ms, "bound": "mfma",
+            "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+            "traffic": None if traffic is None else traffic * len(launch_ms)}
 
 
 def main() -> int:
@@ -424,17 +570,23 @@ def main() -> int:
         print(json.dumps({"copy_bytes": src.numel() * 4, "reads": src.numel() * 4, "writes": src.numel() * 4}))
         return 0
     w = W.WORKLOADS[args.workload]
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)   # before any GPU use
+    also = [x for x in args.also.split(",") if x and x != args.workload]
+    # the oracle baselines run before any GPU use (their pools fork)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    cpu_extra = {} if args.no_cpu_baseline else {name: cpu_baseline(W.WORKLOADS[name], args.cpu_seconds)
+                                                 for name in also}
 
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     main_run = run_workload(w, args.steps, args.warmup)
     extra = {}
-    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+    for name in also:
         r = run_workload(W.WORKLOADS[name], args.steps, args.warmup)
         extra[name] = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                       "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"]}
+                       "pyramid_ms": r["pyramid_ms"], "select_ms": r["select_ms"], "attn_ms": r["attn_ms"],
+                       "roofline": attention_roofline(r), "selection_roofline": kernel_table(r),
+                       "cpu_baseline": cpu_extra.get(name)}
     if not args.no_sweep:
         q_main, k_main, _ = _INPUTS[w.name]
         extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
@@ -453,8 +605,6 @@ def main() -> int:
     _INPUTS.clear()
     if not args.no_decode:
         extra["decode_b64_ctx131072"] = run_decode(W.WORKLOADS["decode_b64_ctx131072"])
-    attn_tflops = main_run["attn_flops"] / (main_run["attn_ms"] * 1e-3) / 1e12
-    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     line = {
         "metric": "prefill tokens/s (select+sparse attn)",
         "value": main_run["tokens_per_s"],
@@ -474,13 +624,13 @@ def main() -> int:
         "pyramid_ms": main_run["pyramid_ms"],
         "select_ms": main_run["select_ms"],
         "attn_ms": main_run["attn_ms"],
-        # attention_bf16_kernel: one sparse_attn_fwd call runs it twice (even, then odd block ids,
-        # for a float32 output), so achieved and traffic are per call, i.e. per pair of launches,
-        # timed with the block packing that the call runs first (about 0.5% of it); flops count
+        # the dominant kernel: attention_bf16_kernel, launched once per pass (even, then odd block
+        # ids, for a float32 output); achieved and traffic are per call (both launches), flops count
         # valid keys only
-        "roofline": {"kernel": "attention_bf16_kernel", "launches": 2 if w.dtype == "bf16" else 1,
-                     "bound": "mfma", "achieved": attn_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": attention_traffic(w.name)},
+        "roofline": attention_roofline(main_run),
+        # every pyramid and selection kernel: duration, compulsory HBM bytes and their fraction of
+        # 8 TB/s, counter traffic where current; the leaf scores also against the bf16 MFMA peak
+        "selection_roofline": kernel_table(main_run),
         "cpu_baseline": cpu,
         "also": extra,
     }

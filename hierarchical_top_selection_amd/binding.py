@@ -48,6 +48,7 @@ _SIGNATURES = {
     "pisa_abi_version": (ctypes.c_int, []),
     "pisa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pisa_last_hip_error": (ctypes.c_int, []),
+    "pisa_stage_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "pisa_pyramid_nodes": (ctypes.c_int64, [ctypes.c_int32]),
     "pisa_pyramid_bytes": (ctypes.c_size_t, [_P(PisaCfg), ctypes.c_int32]),
     "pisa_build_pyramid": (ctypes.c_int, [_P(PisaCfg), PisaTensor, ctypes.c_int32, ctypes.c_int32,
@@ -148,6 +149,22 @@ def _ws_bytes(ws: torch.Tensor) -> int:
 
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+_STAGE_ARRAY = []   # keeps the handle array of stage_events alive until the next call has used it
+
+
+def stage_events(events) -> None:
+    """Hands timing-enabled torch.cuda.Event objects to the next binding call on this thread: the
+    library records events[i] on its stream right after it enqueues its i-th kernel."""
+    handles = []
+    for e in events:
+        if not e.cuda_event:                  # torch creates the event on its first record
+            e.record()
+        handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    _STAGE_ARRAY[:] = [arr]
+    _check("pisa_stage_events", lib().pisa_stage_events(ctypes.cast(arr, ctypes.c_void_p), len(handles)))
 
 
 def make_cfg(batch: int, seq_len: int, n_q_heads: int, n_kv_heads: int, head_dim: int, top_k: int,

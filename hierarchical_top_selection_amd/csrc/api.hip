@@ -14,6 +14,19 @@ using pisa::Levels;
 
 thread_local int g_last_hip_error = 0;
 
+// Stage events handed over by pisa_stage_events, consumed by the calling thread's next entry
+// point: one is recorded on its stream after each kernel it launches.
+thread_local void* const* g_stage_events = nullptr;
+thread_local int g_stage_left = 0;
+
+// Clears the pending stage events when an entry point returns, whether or not it launched.
+struct StageScope {
+  ~StageScope() {
+    g_stage_events = nullptr;
+    g_stage_left = 0;
+  }
+};
+
 constexpr int kMaxSeqSelect = 1000000;     // leaf counters of one window must fit in LDS
 constexpr int kMaxSeq = (1 << 25) - 1;     // packed (token << 6 | slot) fits int32
 // Tokens per Stage-2 clustering window: a window's query rows and the key blocks its
@@ -193,7 +206,31 @@ constexpr int kAttnPasses = 2;
 
 }  // namespace
 
+namespace pisa {
+
+hipError_t launched(hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g_stage_left <= 0) return e;
+  e = hipEventRecord(static_cast<hipEvent_t>(*g_stage_events), s);
+  ++g_stage_events;
+  --g_stage_left;
+  return e;
+}
+
+}  // namespace pisa
+
 extern "C" {
+
+pisa_status pisa_stage_events(void* const* events, int32_t count) {
+  g_stage_events = nullptr;
+  g_stage_left = 0;
+  if (count < 0 || (count > 0 && !events)) return PISA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i)
+    if (!events[i]) return PISA_ERR_INVALID_ARG;
+  g_stage_events = events;
+  g_stage_left = count;
+  return PISA_OK;
+}
 
 int pisa_abi_version(void) { return PISA_ABI_VERSION; }
 
@@ -222,6 +259,7 @@ size_t pisa_pyramid_bytes(const pisa_cfg* cfg, int32_t capacity) {
 
 pisa_status pisa_build_pyramid(const pisa_cfg* cfg, pisa_tensor k, int32_t n, int32_t capacity, float* pyr,
                                void* stream) {
+  StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   if (n < 1 || capacity < n || capacity > kMaxSeq) return PISA_ERR_INVALID_ARG;
@@ -243,6 +281,7 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg) {
 
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr, int32_t* sel,
                                float* sel_u, void* ws, size_t ws_bytes, void* stream) {
+  StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   if (cfg->seq_len > kMaxSeqSelect) return PISA_ERR_UNSUPPORTED;
@@ -321,6 +360,7 @@ size_t pisa_flat_workspace_bytes(const pisa_cfg* cfg) {
 
 pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* pyr, int32_t* sel, float* sel_u,
                              void* ws, size_t ws_bytes, void* stream) {
+  StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   if (cfg->top_k > 16) return PISA_ERR_UNSUPPORTED;
@@ -351,6 +391,7 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg) {
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
                                  void* ws, size_t ws_bytes, void* stream) {
+  StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   const size_t need = pisa_attn_workspace_bytes(cfg);
@@ -396,6 +437,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
                                  const int32_t* sel, pisa_tensor o, pisa_tensor dout, pisa_dtype grad_dtype,
                                  const float* row_lse, pisa_tensor_mut dq, pisa_tensor_mut dk, pisa_tensor_mut dv,
                                  void* ws, size_t ws_bytes, void* stream) {
+  StageScope stages;
   pisa_status st = check_bwd_cfg(cfg);
   if (st != PISA_OK) return st;
   const BwdWorkspace w = bwd_layout(cfg);
@@ -444,6 +486,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
                              pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache, float* pyr,
                              int32_t* sel_out, pisa_tensor_mut o, pisa_dtype o_dtype, void* stream) {
+  StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   if (o_dtype != PISA_F32 && o_dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;

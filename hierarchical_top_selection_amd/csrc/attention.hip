@@ -336,12 +336,12 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
       AttnArgs ap = a;
       ap.pass = pass;
       hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, ap);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = launched(s)) != hipSuccess) return e;
     }
-  } else {
-    hipLaunchKernelGGL((attention_f32_kernel<TO, D>), grid, dim3(256), 0, s, a);
+    return hipSuccess;
   }
-  return hipGetLastError();
+  hipLaunchKernelGGL((attention_f32_kernel<TO, D>), grid, dim3(256), 0, s, a);
+  return launched(s);
 }
 
 template <typename TO>

@@ -526,28 +526,28 @@ hipError_t launch_attention_bwd_t(const BwdArgs& a, hipStream_t s) {
   const dim3 tok_grid(ceil_div(a.n, 4), bhs);
   const int rec_threads = 16 * (D / 8);                     // one token's pieces
   hipLaunchKernelGGL((bwd_tokens_kernel<TD, D>), dim3((unsigned)a.n, bhs), dim3(rec_threads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   const size_t rank_lds = (size_t)(kBwdChunk * a.top_k + m1) * sizeof(int32_t);
   hipLaunchKernelGGL(bwd_rank_kernel, dim3(chunks, bhs), dim3(256), rank_lds, s, a, chunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   const unsigned blk_grid = (unsigned)((blocks + 255) / 256);
   hipLaunchKernelGGL(bwd_colscan_kernel, dim3(blk_grid), dim3(256), 0, s, a, chunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, s, a, blocks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_items_kernel, dim3(blk_grid), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   const int64_t rows = (int64_t)bhs * a.n;
   hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, chunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
 
   hipLaunchKernelGGL((attn_bwd_dq_kernel<TD, D>), tok_grid, dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D>), dim3((unsigned)a.max_items), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   const int64_t fin = blocks * kLeaf * (D / 4);
   hipLaunchKernelGGL((attn_bwd_finish_kernel<D>), dim3((unsigned)((fin + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 template <typename TD>

@@ -103,7 +103,7 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
   const size_t lds = (size_t)(a.n_leaves + 2 * kClusterThreads / 64) * sizeof(int);
   dim3 grid(a.n_windows, a.batch * a.n_kv_heads);
   hipLaunchKernelGGL(cluster_kernel, grid, dim3(kClusterThreads), lds, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 }  // namespace pisa

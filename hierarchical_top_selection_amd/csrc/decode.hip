@@ -337,13 +337,13 @@ hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(a.batch * a.n_kv_heads), dim3(kDecodeWaves * 64), lds, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_update_kernel<T, D>), dim3(a.batch * a.n_kv_heads), dim3(D), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched(s);
   if (e != hipSuccess) return e;
   switch (a.group) {
     case 1: return launch_decode_fused<T, D, 1>(a, s);

@@ -165,13 +165,13 @@ hipError_t launch_flat_t(const FlatArgs& a, hipStream_t s) {
   const int64_t bhs = (int64_t)a.batch * a.n_kv_heads;
   const int64_t q_threads = bhs * ceil_div(a.n, 16) * (D / 16) * 64;
   hipLaunchKernelGGL((flat_qsum_kernel<T, D>), dim3((unsigned)((q_threads + 255) / 256)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched(s);
   if (e != hipSuccess) return e;
   const int64_t k_threads = bhs * ceil_div(ceil_div(a.n, kLeaf), 16) * (D / 16) * 64;
   hipLaunchKernelGGL((flat_kpack_kernel<D>), dim3((unsigned)((k_threads + 255) / 256)), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launched(s)) != hipSuccess) return e;
   hipLaunchKernelGGL((flat_select_kernel<D>), dim3(ceil_div(ceil_div(a.n, 16), 4), (unsigned)bhs), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_flat(const FlatArgs& a, hipStream_t s) {

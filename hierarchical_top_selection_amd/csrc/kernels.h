@@ -172,6 +172,11 @@ struct DecodeArgs {
   Levels lv;                // sizes for length n_ctx + 1, capacity offsets
 };
 
+// Status of the kernel just enqueued on s.  When it launched and the calling thread has stage
+// events pending (pisa_stage_events), the next of them is recorded on s, so a caller can time
+// every kernel of an entry point on the stream it runs on.
+hipError_t launched(hipStream_t s);
+
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

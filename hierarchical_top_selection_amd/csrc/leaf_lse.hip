@@ -215,7 +215,7 @@ hipError_t launch_leaf_t(const LeafArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((leaf_lse_kernel<T, D, 2>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((leaf_lse_kernel<T, D, 0>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s) {

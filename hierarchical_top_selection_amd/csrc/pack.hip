@@ -61,7 +61,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(pack_blocks_kernel<64>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(pack_blocks_kernel<128>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 }  // namespace pisa

@@ -92,11 +92,11 @@ template <typename T, int D>
 hipError_t launch_pyramid_t(const PyramidArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.lv.size[0], kLeavesPerBlock), a.batch * a.n_kv_heads);
   hipLaunchKernelGGL((pyramid_leaves_kernel<T, D>), grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched(s);
   if (e != hipSuccess) return e;
   if (a.lv.count > kInBlockLevels) {
     hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(a.batch * a.n_kv_heads), dim3(1024), 0, s, a);
-    e = hipGetLastError();
+    e = launched(s);
   }
   return e;
 }

@@ -260,7 +260,7 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((route_kernel<T, D, 2>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((route_kernel<T, D, 0>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_split_summaries(const RouteArgs& a, hipStream_t s) {
@@ -270,7 +270,7 @@ hipError_t launch_split_summaries(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(split_summaries_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(split_summaries_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {

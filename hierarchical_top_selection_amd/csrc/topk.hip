@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
   hipLaunchKernelGGL(topk_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 }  // namespace pisa

@@ -35,7 +35,8 @@
  *    pisa_status means nothing was launched, except PISA_ERR_HIP, which means a
  *    launch failed (pisa_last_hip_error() then returns the hipError_t value of
  *    the calling thread's last failure).  No C++ exception crosses the ABI.
- *  - Thread safety: no global mutable state besides the thread-local error code.
+ *  - Thread safety: no global mutable state besides the thread-local error code
+ *    and the thread-local stage events of pisa_stage_events.
  */
 #ifndef PISA_H_
 #define PISA_H_
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 5
+#define PISA_ABI_VERSION 6
 
 typedef enum {
   PISA_OK = 0,
@@ -100,6 +101,21 @@ const char* pisa_status_string(pisa_status status);
 
 /* hipError_t of the calling thread's last failed launch (0 if none). */
 int pisa_last_hip_error(void);
+
+/* Timing hook: hands the calling thread `count` hipEvent_t handles (as void*,
+ * created by the caller) for its NEXT entry-point call, which records
+ * events[i] on its stream right after enqueueing its i-th kernel (in launch
+ * order; events beyond the kernels it launches stay unrecorded) and then drops
+ * the list, also when it returns an error.  Recording the same event twice in
+ * one call is the caller's choice.  The array must stay valid during that
+ * call.  Kernels per call: build_pyramid 1 or 2 (leaves, then the top levels
+ * above 8 leaves); select_blocks 5 or 6 (split summaries for bf16 inputs,
+ * routing, clustering, packing of K for bf16 inputs, leaf LSE, top-K);
+ * sparse_attn_fwd with bf16 inputs 1 + passes (packing of K and V, then one
+ * launch per pass), fp32 inputs 1; decode_step 2 (update, fused step);
+ * select_flat 3.  count = 0 clears the list.  Returns PISA_ERR_INVALID_ARG
+ * for count < 0 or a null array or handle. */
+pisa_status pisa_stage_events(void* const* events, int32_t count);
 
 /* Nodes per (sequence, KV head) of a pyramid with room for `capacity` keys:
  * sum over levels of ceil(capacity / 64), then repeated ceil(/2) down to 1.

@@ -16,10 +16,19 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_symbols()
-    assert len(declared) == 15
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 5
+    assert lib.pisa_abi_version() == 6
+
+
+def test_stage_events_validation(lib):
+    """The timing hook rejects a negative count and null handles; count 0 clears it."""
+    assert lib.pisa_stage_events(None, -1) == 1
+    assert lib.pisa_stage_events(None, 2) == 1
+    arr = (ctypes.c_void_p * 2)(16, None)
+    assert lib.pisa_stage_events(ctypes.cast(arr, ctypes.c_void_p), 2) == 1
+    assert lib.pisa_stage_events(None, 0) == 0
 
 
 def test_status_strings(lib):

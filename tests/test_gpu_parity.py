@@ -294,7 +294,7 @@ def check_prefill_every_token(w: W.Workload, label: str, pool, chunk: int = 512)
     H.assert_mismatch_budget(len(bad), agree.size, label)
     # leaf scores of the selected leaves where the selections agree
     ok = agree[..., None] & (ora_sel >= 0)
-    du = np.abs(sel_u - ora_u)[ok]
+    du = np.abs(sel_u[ok] - ora_u[ok])
     assert np.all(du <= 1e-4 + 1e-5 * np.abs(ora_u[ok])), (label, "leaf scores", float(du.max()))
     assert np.all(np.isneginf(sel_u[agree[..., None] & (ora_sel < 0)]))
     H.log(f"[{label}] max |du| over {int(ok.sum())} selected leaves {du.max():.3g}")
