@@ -63,6 +63,9 @@ _SIGNATURES = {
     "pisa_sparse_attn_fwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
                                             PisaTensor, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
+    "pisa_sparse_attn_fwd_noalloc": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor,
+                                                    ctypes.c_void_p, PisaTensor, ctypes.c_int, ctypes.c_void_p,
+                                                    ctypes.c_void_p]),
     "pisa_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_P(PisaCfg)]),
     "pisa_sparse_attn_bwd": (ctypes.c_int, [_P(PisaCfg), PisaTensor, PisaTensor, PisaTensor, ctypes.c_void_p,
                                             PisaTensor, PisaTensor, ctypes.c_int, ctypes.c_void_p, PisaTensor,
@@ -300,6 +303,37 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
         _tensor(out), _dtype_code(out), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
         ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_len), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20       # PISA_NOALLOC_SCRATCH_BYTES
+
+
+def sparse_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor,
+                            out: torch.Tensor, lse_out: torch.Tensor | None = None, scale: float = 0.0):
+    """`sparse_attn_fwd` through the allocation-free entry point: the caller passes the output (and
+    optionally the row LSE [B, Hq, N] float32) and the workspace is the library's fixed device
+    array; nothing is allocated here either."""
+    B, N, Hq, d = q.shape
+    top_k = sel.shape[-1]
+    Hkv = k.shape[2]
+    _expect("k", k, (B, N, Hkv, d), q.dtype, q.device)
+    _expect("v", v, (B, N, Hkv, d), q.dtype, q.device)
+    cfg = _cfg_from(q, k, top_k, scale)
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.shape != (B, Hkv, N, top_k):
+        raise ValueError("selection must be a contiguous int32 [B, Hkv, N, K] tensor")
+    _expect("out", out, q.shape, None, q.device)
+    _dtype_code(out)
+    if any(_overlap(out, x) for x in (q, k, v, sel)):
+        raise ValueError("out must not overlap q, k, v or the selection")
+    if lse_out is not None:
+        _expect("lse_out", lse_out, (B, Hq, N), torch.float32, q.device)
+        if not lse_out.is_contiguous():
+            raise ValueError("lse_out must be contiguous")
+    _check("pisa_sparse_attn_fwd_noalloc", lib().pisa_sparse_attn_fwd_noalloc(
+        ctypes.byref(cfg), _tensor(q), _tensor(k), _tensor(v), ctypes.c_void_p(sel.data_ptr()),
+        _tensor(out), _dtype_code(out), ctypes.c_void_p(lse_out.data_ptr() if lse_out is not None else 0),
+        _stream(q)))
+    return out
 
 
 def attn_bwd_workspace_bytes(cfg: PisaCfg) -> int:

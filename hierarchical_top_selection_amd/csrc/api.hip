@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attention_bwd.h"
 #include "kernels.h"
 #include "pisa.h"
@@ -388,10 +390,14 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg) {
   return attn_layout(cfg).total;
 }
 
-pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
-                                 void* ws, size_t ws_bytes, void* stream) {
-  StageScope stages;
+}  // extern "C"
+
+namespace {
+
+// Forward attention with the workspace the caller (or the fixed device array) provides.
+pisa_status attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v, const int32_t* sel,
+                     pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse, void* ws, size_t ws_bytes,
+                     void* stream) {
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
   const size_t need = pisa_attn_workspace_bytes(cfg);
@@ -426,6 +432,60 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
   a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = out_bf16;
   return hip_status(pisa::launch_attention(a, (hipStream_t)stream));
+}
+
+// The allocation-free forward's workspace: one fixed array per GPU, held until the process ends.
+// Host code never passes `scratch` itself (in host code its name stands for a host-side stand-in):
+// its device address, queried once per device, is what the kernels get.
+constexpr int kMaxDevices = 64;
+static_assert(PISA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[PISA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's array (null with the HIP error recorded on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip_error = e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  StageScope stages;
+  return attn_fwd(cfg, q, k, v, sel, o, o_dtype, row_lse, ws, ws_bytes, stream);
+}
+
+pisa_status pisa_sparse_attn_fwd_noalloc(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                         const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype,
+                                         float* row_lse, void* stream) {
+  StageScope stages;
+  pisa_status st = check_cfg(cfg);
+  if (st != PISA_OK) return st;
+  const size_t need = pisa_attn_workspace_bytes(cfg);
+  if (need > PISA_NOALLOC_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need && !(ws = scratch_on_current_device())) return PISA_ERR_HIP;
+  return attn_fwd(cfg, q, k, v, sel, o, o_dtype, row_lse, ws, need ? PISA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t pisa_attn_bwd_workspace_bytes(const pisa_cfg* cfg) {

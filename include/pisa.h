@@ -35,8 +35,10 @@
  *    pisa_status means nothing was launched, except PISA_ERR_HIP, which means a
  *    launch failed (pisa_last_hip_error() then returns the hipError_t value of
  *    the calling thread's last failure).  No C++ exception crosses the ABI.
- *  - Thread safety: no global mutable state besides the thread-local error code
- *    and the thread-local stage events of pisa_stage_events.
+ *  - Thread safety: no global mutable state besides the thread-local error code,
+ *    the thread-local stage events of pisa_stage_events and the per-device
+ *    address of the fixed array behind pisa_sparse_attn_fwd_noalloc (set once,
+ *    under a lock).
  */
 #ifndef PISA_H_
 #define PISA_H_
@@ -225,6 +227,29 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Size of the device array behind pisa_sparse_attn_fwd_noalloc (one per GPU). */
+#define PISA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * sparse_attn_fwd_noalloc - for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same computation, arguments and errors as sparse_attn_fwd, but
+ * the workspace is a fixed array of PISA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends; nothing is allocated or freed.  Returns PISA_ERR_WORKSPACE, before
+ * touching the device, when pisa_attn_workspace_bytes(cfg) exceeds
+ * PISA_NOALLOC_SCRATCH_BYTES (128 MiB: e.g. bf16 inputs with d = 128, 16
+ * query heads per KV head and B * H_kv * N up to about 200K tokens), and
+ * PISA_ERR_HIP if the array's device address cannot be obtained.  Every call
+ * on one GPU uses the same array and leaves its contents behind (each call
+ * writes all it reads first, so no clearing is needed): calls that overlap on
+ * one GPU (on several streams or threads) race and must be serialised by the
+ * caller.
+ */
+pisa_status pisa_sparse_attn_fwd_noalloc(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
+                                         const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype,
+                                         float* row_lse, void* stream);
 
 /* Workspace bytes needed by pisa_sparse_attn_bwd for cfg (0 for an unsupported
  * cfg): packed copies of K and V (2 * B * H_kv * ceil(N / 64) * 64 * d * 2

@@ -16,10 +16,22 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_symbols()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.pisa_abi_version() == 6
+
+
+def test_noalloc_forward_refuses_oversized_workloads_before_touching_the_device(lib):
+    """The allocation-free forward attention checks its workspace need against the fixed array first:
+    the 256K workload (168 MB of packed K/V and softmax state) exceeds 128 MiB."""
+    cfg = _cfg(seq_len=262144)
+    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) > binding.NOALLOC_SCRATCH_BYTES
+    good = binding.PisaTensor(4096, 0, 128, 128)
+    assert lib.pisa_sparse_attn_fwd_noalloc(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
+                                            None, None) == 3
+    assert lib.pisa_sparse_attn_fwd_noalloc(ctypes.byref(_cfg(top_k=0)), good, good, good, ctypes.c_void_p(4096),
+                                            good, 0, None, None) == 1
 
 
 def test_stage_events_validation(lib):
