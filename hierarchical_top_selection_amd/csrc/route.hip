@@ -14,12 +14,17 @@
 // leaf stage's packed query layout.
 //
 // Scores need close to single precision (near-ties between candidates are
-// common).  fp32 queries use fp32 summaries on v_mfma_f32_16x16x4_f32.  bf16
-// queries are exact in bf16 and in f16, so each fp32 summary x is split once
-// into hi = bf16(x) and lo = f16((x - hi) 2^10) (the remainder's 8 + 11 bits
-// leave a relative error of about 2^-20 per element) and q . x = q . hi +
-// 2^-10 q . lo runs on the 16-cycle bf16 and f16 16x16x32 MFMAs: 8 instead of
-// 32 fp32 MFMAs per tile, from the same 4 bytes per element.  The kernel
+// common).  fp32 queries use fp32 summaries on v_mfma_f32_16x16x4_f32.  For
+// bf16 queries each fp32 summary x is split once into hi = bf16(x) and lo =
+// f16((x - hi) 2^10) (the remainder's 8 + 11 bits leave a relative error of
+// about 2^-20 per element), and q . x = q . hi + 2^-10 q . lo runs on the
+// 16-cycle bf16 and f16 16x16x32 MFMAs: 8 instead of 32 fp32 MFMAs per tile,
+// from the same 4 bytes per element.  q . hi uses the bf16 query as it is.  The
+// remainder product takes the query in f16, which holds a bf16 value exactly
+// for 2^-14 <= |q| <= 65504; smaller values become f16 subnormals (absolute
+// error <= 2^-25, so at most 2^-35 |lo| per element after the 2^-10 factor) and
+// larger ones are clamped to 65504 (an error of at most 2^-10 |lo| (|q| - 65504)
+// per element, reached only by queries far outside any trained model's range).  The kernel
 // gathers summary rows (8 KB per 16-child tile), so each tile's rows are
 // requested one tile ahead.  The LSE of a candidate's two children is evaluated
 // in base 2 as max + log2(1 + 2^-|diff|) on pre-scaled logits; the mean and mean + var/2 score
@@ -68,7 +73,8 @@ template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 rem
       }
     }
   };
-  // bf16 values are exact in f16 up to its range; larger ones saturate
+  // the remainder product's f16 copy of the query: exact for 2^-14 <= |q| <= 65504, subnormal
+  // below (absolute error <= 2^-25), clamped above
   __device__ static inline void load_q(Q& q, const __bf16* row, int g) {
     q.h.load(row, g);
 #pragma unroll
