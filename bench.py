@@ -247,8 +247,32 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
             "leaf_flops": leaf_flops, "kernel_names": names, "kernel_ms": kernel_ms}
 
 
-def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
-    """Selection latency, hierarchical vs single-level, on prefixes N = 4K .. full of one input.
+def device_inputs(w: W.Workload, n: int, seed: int = 7):
+    """Q and K of n tokens drawn on the device with the workload's recipe (N(0,1), queries + alpha_q u,
+    keys of round(frac * M1) random leaf blocks + alpha_k u, the same fraction of planted blocks as w),
+    rounded to bf16; for lengths whose host draw would take minutes."""
+    import torch
+
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(seed)
+    d = w.head_dim
+    u = torch.randn(d, generator=gen, device="cuda:0")
+    u = u / u.norm()
+    q = torch.randn((w.batch, n, w.n_q_heads, d), generator=gen, device="cuda:0") + w.alpha_q * u
+    k = torch.randn((w.batch, n, w.n_kv_heads, d), generator=gen, device="cuda:0")
+    m1 = -(-n // 64)
+    n_plant = max(1, round(w.plant_blocks / w.n_leaves * m1))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            for j in torch.randperm(m1, generator=gen, device="cuda:0")[:n_plant].tolist():
+                k[b, 64 * j:64 * j + 64, h] += w.alpha_k * u
+    return q.to(torch.bfloat16), k.to(torch.bfloat16)
+
+
+def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5, w: W.Workload | None = None,
+                    longer=(524288, 1000000)) -> dict:
+    """Selection latency, hierarchical vs single-level, on prefixes N = 4K .. full of one input,
+    then at the `longer` lengths on device-drawn inputs of the same recipe (`device_inputs`).
 
     Both sides build the key pyramid (the flat scan reads its leaf means) and then
     select K leaves per token: `select_blocks` (routing + exact leaf LSE + top-K)
@@ -261,9 +285,14 @@ def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
 
     B, N, Hq, d = q.shape
     ns = [n for n in (4096, 8192, 16384, 32768, 65536, 131072, 262144) if n <= N]
-    out = {"K": K, "n": ns, "pisa_select_ms": [], "flat_select_ms": [], "flat_over_pisa": []}
-    for n in ns:
-        qn, kn = q[:, :n], k[:, :n]
+    longer = [n for n in longer if n > N] if w is not None else []
+    out = {"K": K, "n": ns + longer, "device_drawn_from": longer[0] if longer else None,
+           "pisa_select_ms": [], "flat_select_ms": [], "flat_over_pisa": []}
+    for n in ns + longer:
+        if n in longer:
+            qn, kn = device_inputs(w, n)
+        else:
+            qn, kn = q[:, :n], k[:, :n]
         cfg = binding.make_cfg(B, n, Hq, n_kv_heads, d, K, q.dtype)
         ws_h = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
         ws_f = torch.empty(binding.flat_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
@@ -287,7 +316,11 @@ def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5) -> dict:
                 times.append(e0.elapsed_time(e1))
             out[key].append(sorted(times)[len(times) // 2])
         out["flat_over_pisa"].append(out["flat_select_ms"][-1] / out["pisa_select_ms"][-1])
-        del ws_h, ws_f, pyr, sel
+        del ws_h, ws_f, pyr, sel, qn, kn
+        torch.cuda.empty_cache()
+    r = out["flat_over_pisa"]
+    cross = next((i for i in range(1, len(r)) if r[i - 1] < 1.0 <= r[i]), None)
+    out["crossover_between"] = None if cross is None else [out["n"][cross - 1], out["n"][cross]]
     return out
 
 
@@ -589,7 +622,7 @@ def main() -> int:
                        "cpu_baseline": cpu_extra.get(name)}
     if not args.no_sweep:
         q_main, k_main, _ = _INPUTS[w.name]
-        extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8)
+        extra["selection_sweep_k8"] = selection_sweep(q_main, k_main, w.n_kv_heads, K=8, w=w)
         extra["score_variants"] = variant_selection(q_main, k_main, w.n_kv_heads, w.top_k)
     if not args.no_backward:
         q_main, k_main, v_main = _INPUTS[w.name]
