@@ -3,21 +3,22 @@
 // leaf mean and its ancestor path, then a single fused pass that walks every
 // level down to exact leaf scores, keeps K leaves and attends over them.
 //
-// The update runs one workgroup per (b, kvh) with one thread per column and the
-// same pooling functions as the prefill build, so the pyramid stays
-// bit-identical to a rebuild.  The fused kernel is one multi-wave workgroup per
-// (b, kvh): levels are serial, the work inside each level, the candidate leaves
-// and the attended blocks are spread over the waves (see the kernel's comment).
+// One multi-wave workgroup per (b, kvh) does the whole step: first the update,
+// one thread per column with the same pooling functions as the prefill build (so
+// the pyramid stays bit-identical to a rebuild), then the routing levels (serial),
+// with the work inside each level, the candidate leaves and the attended blocks
+// spread over the waves (see the kernel's comment).
 #include "kernels.h"
 #include "pyramid_dev.h"
 
 namespace pisa {
 
+// Update of unit bh by threads c < D (one per column): append the new key and value at n_ctx,
+// recompute the new token's leaf mean and its ancestor path with the pooling of the prefill build,
+// so the pyramid stays bit-identical to a rebuild.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void decode_update_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
+__device__ inline void decode_update_unit(const DecodeArgs& a, int bh, int c) {
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const int c = threadIdx.x;                      // blockDim.x == D
   const int64_t pos = a.n_ctx;
   T* kc = reinterpret_cast<T*>(a.k_cache) + b * a.kc_sb + kvh * a.kc_sh;
   T* vc = reinterpret_cast<T*>(a.v_cache) + b * a.vc_sb + kvh * a.vc_sh;
@@ -75,35 +76,56 @@ constexpr int kDecodeWaves = 8;
 
 // LDS carve-up of the fused kernel (4-byte words).
 struct DecodeLds {
-  int zl, part, us, hstat, ints;
+  int zl, part, us, hstat, prank, ints;
   size_t bytes;
   __host__ __device__ DecodeLds(int G, int width, int D) {
     zl = 0;                                   // width * 64 * G staged leaf logits, then probabilities
     part = zl + width * kLeaf * G;            // kDecodeWaves * G * D partial outputs
     us = part + kDecodeWaves * G * D;         // 64 candidate scores
     hstat = us + 64;                          // per-head max and 1 / sum
-    ints = hstat + 2 * G;                     // cand[64], keep[64], selv[64], sels[64], misc[4]
+    prank = hstat + 2 * G;                    // kDecodeWaves * 64 partial ranks
+    ints = prank + kDecodeWaves * 64;         // cand[64], keep[64], selv[64], sels[64], misc[4]
     bytes = (size_t)(ints + 4 * 64 + 4) * 4;
   }
 };
 
-// Wave 0: keep candidates by exact rank (u descending, index ascending) or, when at most K
-// are valid, all of them.  Returns this lane's keep flag (lane i = slot i).
-__device__ inline bool decode_keep(const int* cand, const float* us, int nslots, int nvalid, int K, int lane) {
+// Order-preserving key of a candidate for the ranking (score descending, index ascending): the
+// score's bits made order-preserving (-0 as +0) above the complemented index; empty slots are 0.
+__device__ inline uint64_t rank_key(float u, int c) {
+  const uint32_t ub = __builtin_bit_cast(uint32_t, u + 0.f);
+  const uint32_t hi = c >= 0 ? ((ub & 0x80000000u) ? ~ub : (ub | 0x80000000u)) : 0u;
+  const uint32_t lo = c >= 0 ? 0xffffffffu - (uint32_t)c : 0u;
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Ranking shared by the waves: wave w counts, for every slot (lane), how many of the slots
+// [8 w, 8 w + 8) beat it; the slots' scores and indices are read from LDS (broadcast reads).
+__device__ inline void decode_rank_partial(const int* cand, const float* us, int nslots, int* prank, int wave,
+                                           int lane) {
+  const uint64_t mine = lane < nslots ? rank_key(us[lane], cand[lane]) : 0ull;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 64 / kDecodeWaves; ++i) {
+    const int j = wave * (64 / kDecodeWaves) + i;
+    if (j < nslots) cnt += (int)(rank_key(us[j], cand[j]) > mine);
+  }
+  prank[wave * 64 + lane] = cnt;
+}
+
+// Wave 0: keep candidates by exact rank (u descending, index ascending), the sum of the waves'
+// partial counts, or, when at most K are valid, all of them.  Returns this lane's keep flag
+// (lane i = slot i).
+__device__ inline bool decode_keep(const int* cand, const int* prank, int nslots, int nvalid, int K, int lane) {
   const int ci = lane < nslots ? cand[lane] : -1;
   if (nvalid <= K) return ci >= 0;
-  const float ui = lane < nslots ? us[lane] : kNegInf;
   int rank = 0;
-  for (int j = 0; j < nslots; ++j) {
-    const float uj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ui), j));
-    const int cj = __builtin_amdgcn_readlane(ci, j);
-    rank += (int)((cj >= 0) & ((uj > ui) | ((uj == ui) & (cj < ci))));
-  }
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) rank += prank[w * 64 + lane];
   return ci >= 0 && rank < K;
 }
 
 template <typename T, typename TO, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void decode_fused_kernel(
     DecodeArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
   extern __shared__ __align__(16) float smem[];
@@ -118,6 +140,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
   int* selv = keep + 64;               // selected leaf ids, ascending
   int* sels = selv + 64;               // their candidate slots
   int* misc = sels + 64;               // [0] slots, [1] valid, [2] selected
+  int* prank = reinterpret_cast<int*>(smem + L.prank);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -129,6 +152,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
   const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + (int64_t)(kvh * G + (head_ok ? col : 0)) * a.q_sh;
   const float* pyr = a.pyr + (int64_t)bh * a.lv.nodes * D;
 
+  // ---- update of this unit (its rows and nodes only), then routing in the same workgroup: the
+  // barrier makes the new key, value and path visible to every wave (one CU, one L1)
+  if (tid < D) decode_update_unit<T, D>(a, bh, tid);
   if (tid < 64) cand[tid] = tid == 0 ? 0 : -1;  // A^(L) = {root}
   if (tid == 0) { misc[0] = 1; misc[1] = 1; }
   __syncthreads();
@@ -162,8 +188,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
       }
     }
     __syncthreads();
+    if (nvalid > K) {
+      decode_rank_partial(cand, us, nslots, prank, wave, lane);
+      __syncthreads();
+    }
     if (wave == 0) {
-      const bool kp = decode_keep(cand, us, nslots, nvalid, K, lane);
+      const bool kp = decode_keep(cand, prank, nslots, nvalid, K, lane);
       const int ci = lane < nslots ? cand[lane] : -1;
       const uint64_t kept = __ballot(kp);
       const int m = __popcll(kept);
@@ -248,8 +278,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
     if (lane == 15) us[slot] = u;
   }
   __syncthreads();
+  if (nvalid > K) {
+    decode_rank_partial(cand, us, nslots, prank, wave, lane);
+    __syncthreads();
+  }
   if (wave == 0) {
-    const bool kp = decode_keep(cand, us, nslots, nvalid, K, lane);
+    const bool kp = decode_keep(cand, prank, nslots, nvalid, K, lane);
     const int c = kp ? cand[lane] : 0x7fffffff;
     int pos = 0;                                        // ascending leaf order among the kept
     for (int j = 0; j < 64; ++j) pos += __builtin_amdgcn_readlane(c, j) < c;
@@ -282,31 +316,44 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_fused_kernel(
   // ---- P V: one selected block per wave, 16 of its value rows in flight at a time (more rows, or
   // a register cap for more waves per SIMD, measured slower)
   constexpr int kCols = D / 64;                         // value columns per lane
-  constexpr int kRows = 16;
+  constexpr int kRows = 8;
   float accv[G][kCols];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int c = 0; c < kCols; ++c) accv[h][c] = 0.f;
   const T* vbase = reinterpret_cast<const T*>(a.v_cache) + b * a.vc_sb + kvh * a.vc_sh + lane * kCols;
-  for (int j = wave; j < nsel; j += kDecodeWaves) {
-    const int slot = sels[j];
-    const int first = selv[j] * kLeaf;
-    for (int r0 = 0; r0 < kLeaf; r0 += kRows) {
-      float vv[kRows][kCols];
+  // This wave's blocks j = wave, wave + 8, ... walked as one stream of 16-row chunks; the next
+  // chunk's value rows are requested before the current chunk's products (two buffers).  The
+  // products run chunk by chunk and row by row, so the order of the sums is the plain one.
+  constexpr int kChunks = kLeaf / kRows;
+  const int n_chunks = (nsel > wave ? (nsel - wave + kDecodeWaves - 1) / kDecodeWaves : 0) * kChunks;
+  auto load_chunk = [&](int ci, T (&buf)[kRows][kCols]) {
+    const int first = selv[wave + (ci / kChunks) * kDecodeWaves] * kLeaf + (ci % kChunks) * kRows;
 #pragma unroll
-      for (int i = 0; i < kRows; ++i)                   // keys past t: clamped row, probability 0
+    for (int i = 0; i < kRows; ++i)                     // keys past t: clamped row, probability 0
 #pragma unroll
-        for (int c = 0; c < kCols; ++c) vv[i][c] = to_f32(vbase[(int64_t)min(first + r0 + i, t) * a.vc_st + c]);
+      for (int c = 0; c < kCols; ++c) buf[i][c] = vbase[(int64_t)min(first + i, t) * a.vc_st + c];
+  };
+  auto fma_chunk = [&](int ci, const T (&buf)[kRows][kCols]) {
+    const int slot = sels[wave + (ci / kChunks) * kDecodeWaves];
+    const int r0 = (ci % kChunks) * kRows;
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        const float* p = &zl[(slot * kLeaf + r0 + i) * G];
+    for (int i = 0; i < kRows; ++i) {
+      const float* p = &zl[(slot * kLeaf + r0 + i) * G];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int c = 0; c < kCols; ++c) accv[h][c] = fmaf(p[h], vv[i][c], accv[h][c]);
-      }
+        for (int c = 0; c < kCols; ++c) accv[h][c] = fmaf(p[h], to_f32(buf[i][c]), accv[h][c]);
     }
+  };
+  T vb0[kRows][kCols], vb1[kRows][kCols];
+  if (n_chunks > 0) load_chunk(0, vb0);
+  for (int ci = 0; ci < n_chunks; ci += 2) {            // n_chunks is a multiple of kChunks (even)
+    load_chunk(ci + 1, vb1);
+    fma_chunk(ci, vb0);
+    if (ci + 2 < n_chunks) load_chunk(ci + 2, vb0);
+    fma_chunk(ci + 1, vb1);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -342,9 +389,6 @@ hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_update_kernel<T, D>), dim3(a.batch * a.n_kv_heads), dim3(D), 0, s, a);
-  hipError_t e = launched(s);
-  if (e != hipSuccess) return e;
   switch (a.group) {
     case 1: return launch_decode_fused<T, D, 1>(a, s);
     case 2: return launch_decode_fused<T, D, 2>(a, s);

@@ -114,7 +114,7 @@ int pisa_last_hip_error(void);
  * above 8 leaves); select_blocks 5 or 6 (split summaries for bf16 inputs,
  * routing, clustering, packing of K for bf16 inputs, leaf LSE, top-K);
  * sparse_attn_fwd with bf16 inputs 1 + passes (packing of K and V, then one
- * launch per pass), fp32 inputs 1; decode_step 2 (update, fused step);
+ * launch per pass), fp32 inputs 1; decode_step 1;
  * select_flat 3.  count = 0 clears the list.  Returns PISA_ERR_INVALID_ARG
  * for count < 0 or a null array or handle. */
 pisa_status pisa_stage_events(void* const* events, int32_t count);
