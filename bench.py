@@ -584,6 +584,8 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-gradient record")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the hierarchical vs single-level selection sweep (K = 8, N = 4K .. the workload's N)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the decode record (for profiling it alone) and print it as one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times), for scaling HBM byte counters")
     args = ap.parse_args()
@@ -601,6 +603,9 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 4, "reads": src.numel() * 4, "writes": src.numel() * 4}))
+        return 0
+    if args.decode_only:
+        print(json.dumps({"decode_b64_ctx131072": run_decode(W.WORKLOADS["decode_b64_ctx131072"])}))
         return 0
     w = W.WORKLOADS[args.workload]
     also = [x for x in args.also.split(",") if x and x != args.workload]
