@@ -445,7 +445,8 @@ def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
     """Decode throughput: `decode_steps` steps of every sequence after a prebuilt context.
 
     The 2 x 17 GB bf16 caches are drawn on the device with a seeded torch generator
-    (N(0, 1), like the workload's recipe; drawing them on the host would take minutes).
+    (N(0, 1), like the workload's recipe; drawing them on the host would take minutes) and laid
+    out head-major.
     One untimed pass of all steps runs first; the pyramid is then rebuilt for the
     context length, so the timed pass starts from the same state.
     """
@@ -457,8 +458,10 @@ def run_decode(w: W.Workload, warmup_passes: int = 1) -> dict:
     cap = n0 + S
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(w.seed)
-    kc = torch.randn((B, cap, Hkv, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
-    vc = torch.randn((B, cap, Hkv, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
+    # head-major caches ([B, Hkv, cap, d] in memory, viewed as [B, cap, Hkv, d]): each (sequence,
+    # KV head) keeps its keys and values contiguous, so a leaf block is one 16 KB run
+    kc = torch.randn((B, Hkv, cap, d), generator=gen, device="cuda:0", dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    vc = torch.randn((B, Hkv, cap, d), generator=gen, device="cuda:0", dtype=torch.bfloat16).permute(0, 2, 1, 3)
     qs = torch.randn((S, B, Hq, d), generator=gen, device="cuda:0", dtype=torch.bfloat16)
     ks = kc[:, n0:].permute(1, 0, 2, 3).contiguous()          # the appended tokens, [S, B, Hkv, d]
     vs = vc[:, n0:].permute(1, 0, 2, 3).contiguous()

@@ -303,7 +303,11 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
  *   n_ctx             : keys already in the cache (same for every sequence)
  *   q                 : [B][H_q][d]    (stride_t ignored)
  *   k_new, v_new      : [B][H_kv][d]   (stride_t ignored)
- *   k_cache, v_cache  : [B][capacity][H_kv][d], updated in place
+ *   k_cache, v_cache  : [B][capacity][H_kv][d] by their strides, updated in place.  Any
+ *                       strides with d contiguous; a head-major cache (stride_t = d,
+ *                       stride_h = capacity * d) keeps each leaf's 64 keys in one
+ *                       contiguous 16 KB run at d = 128 and bf16, which the leaf
+ *                       scoring reads faster than rows 2 KB apart (token-major, 8 KV heads)
  *   pyr               : pyramid of the cache (capacity layout), updated in place
  *   sel_out           : optional int32 [B][H_kv][K] (NULL to skip)
  *   o                 : [B][H_q][d] output of element type o_dtype (stride_t ignored)

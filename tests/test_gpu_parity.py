@@ -405,7 +405,7 @@ def test_decode_from_a_single_key():
 @pytest.mark.timeout(1200)
 def test_decode_full_launch_b64(oracle_workers):
     """The 131072-token decode workload as the bench launches it: 64 sequences x 8 KV heads in every
-    step, all 256 steps.  Sequences 0, 31 and 63 hold the seeded contexts and tokens and are checked
+    step, all 256 steps, head-major caches.  Sequences 0, 31 and 63 hold the seeded contexts and tokens and are checked
     on every KV head and step against the oracle (run in the forked pool); the other sequences are
     filled on the device.  The incremental pyramid equals a rebuild bit for bit for all 64."""
     import oracle_pool
@@ -420,8 +420,9 @@ def test_decode_full_launch_b64(oracle_workers):
     H.log(f"[decode_b64] caches B={B} cap={cap} Hkv={Hkv} d={d}; checked sequences {checked}")
     gen = torch.Generator(device=H.DEV)
     gen.manual_seed(4)
-    kc = torch.randn((B, cap, Hkv, d), generator=gen, device=H.DEV, dtype=torch.bfloat16)
-    vc = torch.randn((B, cap, Hkv, d), generator=gen, device=H.DEV, dtype=torch.bfloat16)
+    # head-major caches viewed as [B, cap, Hkv, d], the layout the bench times
+    kc = torch.randn((B, Hkv, cap, d), generator=gen, device=H.DEV, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    vc = torch.randn((B, Hkv, cap, d), generator=gen, device=H.DEV, dtype=torch.bfloat16).permute(0, 2, 1, 3)
     qs = torch.randn((S, B, Hq, d), generator=gen, device=H.DEV, dtype=torch.bfloat16)
     ks = torch.randn((S, B, Hkv, d), generator=gen, device=H.DEV, dtype=torch.bfloat16)
     vs = torch.randn((S, B, Hkv, d), generator=gen, device=H.DEV, dtype=torch.bfloat16)
