@@ -172,6 +172,11 @@ def decode_step_bytes(w: W.Workload, n_ctx: int) -> int:
     return per * w.batch * w.n_kv_heads
 
 
+# kernels that choose and build the attention passes' token order (up to 16384 leaf blocks)
+ORDER_KERNELS = ["order_clear_kernel", "order_share_kernel", "order_hist_kernel", "order_keys_kernel",
+                 "order_scan_kernel", "order_scatter_kernel"]
+
+
 def stage_kernels(w: W.Workload) -> dict:
     """Kernels each entry point launches, in launch order, for a prefill workload (their names)."""
     bf16 = w.dtype == "bf16"
@@ -180,8 +185,8 @@ def stage_kernels(w: W.Workload) -> dict:
         "pyramid": ["pyramid_leaves_kernel"] + (["pyramid_top_kernel"] if levels > 4 else []),
         "select": (["split_summaries_kernel"] if bf16 else []) + ["route_kernel", "cluster_kernel"]
                   + (["pack_blocks_kernel"] if bf16 else []) + ["leaf_lse_kernel", "topk_kernel"],
-        "attention": (["pack_blocks_kernel", "attention_bf16_kernel", "attention_bf16_kernel"] if bf16
-                      else ["attention_f32_kernel"]),
+        "attention": (["pack_blocks_kernel"] + (ORDER_KERNELS if level_sizes(w.seq_len)[0] <= 16384 else [])
+                      + ["attention_bf16_kernel", "attention_bf16_kernel"] if bf16 else ["attention_f32_kernel"]),
     }
 
 

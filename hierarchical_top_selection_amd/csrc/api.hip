@@ -183,28 +183,43 @@ pisa_status check_bwd_cfg(const pisa_cfg* c) {
   return PISA_OK;
 }
 
-// Attention workspace (bf16 inputs): packed K blocks, packed V blocks, and the (m, l) pair of
-// every (b, kvh, token, head) carried between the two passes of a float32-output call.
+constexpr int kAttnPasses = 2;
+constexpr int kOrderMaxLeaves = 16384;       // the order kernels keep per-leaf counters in LDS
+
+// Attention workspace (bf16 inputs): packed K blocks, packed V blocks, the (m, l) pair of every
+// (b, kvh, token, head) carried between the two passes of a float32-output call, and, up to
+// kOrderMaxLeaves leaf blocks, the arrays of the passes' token order (OrderArgs): block counts,
+// key counts, two 64-bit statistics, the tokens' keys and the order itself (sizes 0 beyond that).
 struct AttnWorkspace {
-  size_t kpack, vpack, part_ml, total;
+  size_t kpack, vpack, part_ml, hist, keycnt, stats, keys, order, total;
 };
 
 AttnWorkspace attn_layout(const pisa_cfg* c) {
   AttnWorkspace w;
   const int64_t m1 = (c->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
-  const size_t pack = align256((size_t)c->batch * c->n_kv_heads * m1 * pisa::kLeaf * c->head_dim * 2);
+  const int64_t bh = (int64_t)c->batch * c->n_kv_heads;
+  const size_t pack = align256((size_t)bh * m1 * pisa::kLeaf * c->head_dim * 2);
   w.kpack = 0;
   w.vpack = pack;
   w.part_ml = 2 * pack;
-  w.total = w.part_ml + align256((size_t)c->batch * c->n_q_heads * c->seq_len * 2 * sizeof(float));
+  w.hist = w.part_ml + align256((size_t)c->batch * c->n_q_heads * c->seq_len * 2 * sizeof(float));
+  const bool ordered = m1 <= kOrderMaxLeaves;
+  w.keycnt = w.hist + (ordered ? align256((size_t)bh * m1 * 4) : 0);
+  w.stats = w.keycnt + (ordered ? align256((size_t)kAttnPasses * bh * (m1 + 1) * 4) : 0);
+  w.keys = w.stats + (ordered ? 256 : 0);
+  w.order = w.keys + (ordered ? align256((size_t)kAttnPasses * bh * c->seq_len * 4) : 0);
+  w.total = w.order + (ordered ? align256((size_t)kAttnPasses * bh * c->seq_len * 4) : 0);
+  if (!ordered) w.hist = w.keycnt = w.stats = w.keys = w.order = 0;
   return w;
 }
+
+// Whether the attention workspace holds the token-order arrays.
+bool attn_has_order(const pisa_cfg* c) { return attn_layout(c).order != 0; }
 
 // Passes of a bf16-input attention call: the blocks are split into even and odd ids when the
 // output is float32 (the output rows carry the state between them).  Each pass's gathers then
 // touch half of the blocks, so more of their reads hit the L2 (0.55 against 0.48 at N = 262144): the
 // call takes 8.6 ms against 9.4 ms in one pass there, and 4.9 against 5.7 ms at N = 32768.
-constexpr int kAttnPasses = 2;
 
 }  // namespace
 
@@ -428,6 +443,23 @@ pisa_status attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_ten
   }
   a.pass = 0;
   a.n_passes = (need && !out_bf16) ? kAttnPasses : 1;
+  a.ord = pisa::OrderArgs{};
+  if (need && attn_has_order(cfg)) {
+    const AttnWorkspace w = attn_layout(cfg);
+    char* base = static_cast<char*>(ws);
+    a.ord.sel = sel;
+    a.ord.hist = reinterpret_cast<int32_t*>(base + w.hist);
+    a.ord.keycnt = reinterpret_cast<int32_t*>(base + w.keycnt);
+    a.ord.stats = reinterpret_cast<unsigned long long*>(base + w.stats);
+    a.ord.keys = reinterpret_cast<int32_t*>(base + w.keys);
+    a.ord.order = reinterpret_cast<int32_t*>(base + w.order);
+    a.ord.bh = cfg->batch * cfg->n_kv_heads;
+    a.ord.n = cfg->seq_len;
+    a.ord.m1 = (cfg->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
+    a.ord.top_k = cfg->top_k;
+    a.ord.n_passes = a.n_passes;
+    a.ord.hot_cut = 4 * pisa::kLeaf * cfg->top_k;
+  }
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;
   a.head_dim = cfg->head_dim; a.n = cfg->seq_len; a.top_k = cfg->top_k;
   a.scale = resolve_scale(cfg); a.bf16 = cfg->dtype == PISA_BF16; a.out_bf16 = out_bf16;

@@ -104,9 +104,19 @@ template <typename TO, int D>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   typedef FragBF16<D> Frag;
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.n) return;
   const int bh = blockIdx.y;
+  int t;
+  if (a.ord.order && order_sorted(a.ord.stats)) {
+    // the pass's sorted order (order.hip), cut into kXcds contiguous slices: XCD x walks the x-th
+    // slice in time order (the grid's x size is a multiple of kXcds)
+    const int slice = gridDim.x / kXcds;
+    const int pos = ((blockIdx.x % kXcds) * slice + blockIdx.x / kXcds) * 4 + wave;
+    if (pos >= a.n) return;
+    t = __builtin_amdgcn_readfirstlane(a.ord.order[((int64_t)a.pass * a.ord.bh + bh) * a.n + pos]);
+  } else {
+    t = blockIdx.x * 4 + wave;
+    if (t >= a.n) return;
+  }
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int g = lane >> 4, col = lane & 15;
   const int m1 = ceil_div(a.n, kLeaf);
@@ -332,10 +342,15 @@ hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
     p.batch = a.batch; p.n_kv_heads = a.n_kv_heads; p.head_dim = D; p.n = a.n;
     hipError_t e = launch_pack(p, s);
     if (e != hipSuccess) return e;
+    dim3 grid_bf16 = grid;
+    if (a.ord.order) {
+      if ((e = launch_order(a.ord, s)) != hipSuccess) return e;
+      grid_bf16.x = kXcds * ceil_div(grid.x, kXcds);
+    }
     for (int pass = 0; pass < a.n_passes; ++pass) {
       AttnArgs ap = a;
       ap.pass = pass;
-      hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid, dim3(256), 0, s, ap);
+      hipLaunchKernelGGL((attention_bf16_kernel<TO, D>), grid_bf16, dim3(256), 0, s, ap);
       if ((e = launched(s)) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -83,6 +83,29 @@ struct TopkArgs {
   int batch, n_kv_heads, n, width, top_k;
 };
 
+// Token order of the attention passes (order.hip): workspace arrays; order == nullptr means the
+// natural order.
+struct OrderArgs {
+  const int32_t* sel;           // [bh][n][top_k] selections
+  int32_t* hist;                // [bh][m1] block selection counts
+  int32_t* keycnt;              // [n_passes][bh][m1 + 1] key counts, then cursors
+  int32_t* keys;                // [n_passes][bh][n] each token's key in each pass
+  unsigned long long* stats;    // [0] valid entries, [1] of them also listed by the previous token
+  int32_t* order;               // [n_passes][bh][n] tokens in each pass's visiting order
+  int bh, n, m1, top_k, n_passes;
+  int hot_cut;                  // a block selected more often than this is hot
+};
+
+// The attention takes the sorted order when the selections' blocks are listed by the previous
+// token less than a quarter of the time (stats: valid entries, entries also in the previous row).
+__device__ inline bool order_sorted(const unsigned long long* stats) {
+  const unsigned long long entries = stats[0], overlap = stats[1];
+  return entries > 0 && overlap * 4 < entries;
+}
+
+// Workgroup L of a launch runs on XCD L % kXcds.
+constexpr int kXcds = 8;
+
 struct AttnArgs {
   const void* q;
   int64_t q_sb, q_st, q_sh;
@@ -102,11 +125,15 @@ struct AttnArgs {
   // workspace); the next pass resumes from it.
   int pass, n_passes;
   float* part_ml;
+  // bf16 inputs: the visiting order of each pass's tokens and the statistics that choose between
+  // it and the natural order (ord.order == nullptr: natural order, no order kernels)
+  OrderArgs ord;
   int batch, n_kv_heads, group, head_dim, n, top_k;
   float scale;
   bool bf16;             // element type of q, k, v
   bool out_bf16;         // element type of o
 };
+
 
 // Packed 64-key blocks for bf16 K and V: every MFMA fragment of a block is one contiguous
 // 1 KB run in lane order (lane l = 16 g + col holds 16 bytes), so a fragment load reads whole
@@ -186,6 +213,10 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 hipError_t launch_leaf_lse(const LeafArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Fills a.order and a.stats for the attention passes (counters cleared first).
+hipError_t launch_order(const OrderArgs& a, hipStream_t s);
+size_t order_hist_lds_bytes(int m1);
+size_t order_keys_lds_bytes(int m1, int n_passes);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_flat(const FlatArgs& a, hipStream_t s);
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 6
+#define PISA_ABI_VERSION 7
 
 typedef enum {
   PISA_OK = 0,
@@ -113,7 +113,9 @@ int pisa_last_hip_error(void);
  * call.  Kernels per call: build_pyramid 1 or 2 (leaves, then the top levels
  * above 8 leaves); select_blocks 5 or 6 (split summaries for bf16 inputs,
  * routing, clustering, packing of K for bf16 inputs, leaf LSE, top-K);
- * sparse_attn_fwd with bf16 inputs 1 + passes (packing of K and V, then one
+ * sparse_attn_fwd with bf16 inputs 1 + passes, or 7 + passes up to 16384 leaf
+ * blocks (packing of K and V; the six kernels of the passes' token order:
+ * clear, adjacent-token share, block counts, keys, scan, scatter; then one
  * launch per pass), fp32 inputs 1; decode_step 1;
  * select_flat 3.  count = 0 clears the list.  Returns PISA_ERR_INVALID_ARG
  * for count < 0 or a null array or handle. */
@@ -199,7 +201,11 @@ pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* py
  * rounded up to 256 bytes), followed by B * H_q * N * 8 bytes (rounded up to
  * 256) for the softmax state carried between the two passes of a float32-output
  * call (even block ids, then odd ones; the output rows hold the partial sums
- * between them); fp32 inputs need none (0). */
+ * between them), then, up to 16384 leaf blocks (N <= 1048576), the arrays that
+ * order each pass's tokens: B * H_kv * ceil(N / 64) block counts, 2 * B * H_kv *
+ * (ceil(N / 64) + 1) key counts, two 64-bit statistics, 2 * B * H_kv * N token
+ * keys and 2 * B * H_kv * N token positions (4 bytes each, every array rounded
+ * up to 256); fp32 inputs need none (0). */
 size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
 
 /*
@@ -223,6 +229,13 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  *             normaliser of each row's softmax
  *   ws      : workspace of >= pisa_attn_workspace_bytes(cfg) bytes (may be NULL
  *             when that is 0), 256-byte aligned
+ * With bf16 inputs the passes visit tokens either in position order or, when
+ * the selections' blocks are listed by the previous token less than a quarter
+ * of the time (measured on the device, per call), sorted by each token's
+ * smallest block of the pass selected at most 4 * 64 * K times, in eight
+ * contiguous slices, one per XCD, so tokens sharing such a block meet in one L2.
+ * Either way every row is computed from its own selection alone: the outputs
+ * are the same bit for bit.
  */
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
                                  const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,

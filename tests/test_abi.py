@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_abi_version() == 6
+    assert lib.pisa_abi_version() == 7
 
 
 def test_noalloc_forward_refuses_oversized_workloads_before_touching_the_device(lib):
@@ -109,9 +109,15 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
     # output element type must be float32 or bfloat16
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 5,
                                     None, ctypes.c_void_p(4096), 1 << 30, None) == 1
-    # bf16 attention needs its workspace: packed K and V blocks, then the (m, l) pair of every
-    # (token, query head) carried between the two passes of a float32-output call
-    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == 2 * 4096 * 128 * 2 + 16 * 4096 * 2 * 4
+    # bf16 attention needs its workspace: packed K and V blocks, the (m, l) pair of every
+    # (token, query head) carried between the two passes of a float32-output call, then the token
+    # order of the passes (block counts, key counts, two 64-bit statistics, the tokens' keys and
+    # their positions, two passes each), each array rounded up to 256 bytes
+    up = lambda x: -(-x // 256) * 256
+    m1 = 4096 // 64
+    want = (2 * 4096 * 128 * 2 + 16 * 4096 * 2 * 4 + up(m1 * 4) + up(2 * (m1 + 1) * 4) + 256
+            + 2 * up(2 * 4096 * 4))
+    assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == want
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
                                     None, None, 0, None) == 3
 
