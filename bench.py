@@ -174,7 +174,7 @@ def decode_step_bytes(w: W.Workload, n_ctx: int) -> int:
 
 # kernels that choose and build the attention passes' token order (up to 16384 leaf blocks)
 ORDER_KERNELS = ["order_clear_kernel", "order_share_kernel", "order_hist_kernel", "order_keys_kernel",
-                 "order_scan_kernel", "order_scatter_kernel"]
+                 "order_prefix_kernel", "order_keyscan_kernel", "order_scatter_kernel"]
 
 
 def stage_kernels(w: W.Workload) -> dict:

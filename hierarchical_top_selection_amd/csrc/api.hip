@@ -189,9 +189,10 @@ constexpr int kOrderMaxLeaves = 16384;       // the order kernels keep per-leaf 
 // Attention workspace (bf16 inputs): packed K blocks, packed V blocks, the (m, l) pair of every
 // (b, kvh, token, head) carried between the two passes of a float32-output call, and, up to
 // kOrderMaxLeaves leaf blocks, the arrays of the passes' token order (OrderArgs): block counts,
-// key counts, two 64-bit statistics, the tokens' keys and the order itself (sizes 0 beyond that).
+// key counts per chunk of kOrderChunk tokens, key totals, two 64-bit statistics, the tokens' keys and
+// the order itself (sizes 0 beyond that).
 struct AttnWorkspace {
-  size_t kpack, vpack, part_ml, hist, keycnt, stats, keys, order, total;
+  size_t kpack, vpack, part_ml, hist, keycnt, keytot, stats, keys, order, total;
 };
 
 AttnWorkspace attn_layout(const pisa_cfg* c) {
@@ -205,11 +206,13 @@ AttnWorkspace attn_layout(const pisa_cfg* c) {
   w.hist = w.part_ml + align256((size_t)c->batch * c->n_q_heads * c->seq_len * 2 * sizeof(float));
   const bool ordered = m1 <= kOrderMaxLeaves;
   w.keycnt = w.hist + (ordered ? align256((size_t)bh * m1 * 4) : 0);
-  w.stats = w.keycnt + (ordered ? align256((size_t)kAttnPasses * bh * (m1 + 1) * 4) : 0);
+  const int64_t chunks = (c->seq_len + pisa::kOrderChunk - 1) / pisa::kOrderChunk;
+  w.keytot = w.keycnt + (ordered ? align256((size_t)kAttnPasses * bh * (m1 + 1) * chunks * 4) : 0);
+  w.stats = w.keytot + (ordered ? align256((size_t)kAttnPasses * bh * (m1 + 1) * 4) : 0);
   w.keys = w.stats + (ordered ? 256 : 0);
   w.order = w.keys + (ordered ? align256((size_t)kAttnPasses * bh * c->seq_len * 4) : 0);
   w.total = w.order + (ordered ? align256((size_t)kAttnPasses * bh * c->seq_len * 4) : 0);
-  if (!ordered) w.hist = w.keycnt = w.stats = w.keys = w.order = 0;
+  if (!ordered) w.hist = w.keycnt = w.keytot = w.stats = w.keys = w.order = 0;
   return w;
 }
 
@@ -450,6 +453,7 @@ pisa_status attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_ten
     a.ord.sel = sel;
     a.ord.hist = reinterpret_cast<int32_t*>(base + w.hist);
     a.ord.keycnt = reinterpret_cast<int32_t*>(base + w.keycnt);
+    a.ord.keytot = reinterpret_cast<int32_t*>(base + w.keytot);
     a.ord.stats = reinterpret_cast<unsigned long long*>(base + w.stats);
     a.ord.keys = reinterpret_cast<int32_t*>(base + w.keys);
     a.ord.order = reinterpret_cast<int32_t*>(base + w.order);
@@ -458,6 +462,7 @@ pisa_status attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_ten
     a.ord.m1 = (cfg->seq_len + pisa::kLeaf - 1) / pisa::kLeaf;
     a.ord.top_k = cfg->top_k;
     a.ord.n_passes = a.n_passes;
+    a.ord.n_chunks = (cfg->seq_len + pisa::kOrderChunk - 1) / pisa::kOrderChunk;
     a.ord.hot_cut = 4 * pisa::kLeaf * cfg->top_k;
   }
   a.batch = cfg->batch; a.n_kv_heads = cfg->n_kv_heads; a.group = cfg->n_q_heads / cfg->n_kv_heads;

@@ -88,11 +88,13 @@ struct TopkArgs {
 struct OrderArgs {
   const int32_t* sel;           // [bh][n][top_k] selections
   int32_t* hist;                // [bh][m1] block selection counts
-  int32_t* keycnt;              // [n_passes][bh][m1 + 1] key counts, then cursors
+  int32_t* keycnt;              // [n_passes][bh][m1 + 1][n_chunks] key counts per chunk, then their prefix
+  int32_t* keytot;              // [n_passes][bh][m1 + 1] key totals, then the first position of each key
   int32_t* keys;                // [n_passes][bh][n] each token's key in each pass
   unsigned long long* stats;    // [0] valid entries, [1] of them also listed by the previous token
   int32_t* order;               // [n_passes][bh][n] tokens in each pass's visiting order
   int bh, n, m1, top_k, n_passes;
+  int n_chunks;                 // chunks of kOrderChunk tokens
   int hot_cut;                  // a block selected more often than this is hot
 };
 
@@ -102,6 +104,9 @@ __device__ inline bool order_sorted(const unsigned long long* stats) {
   const unsigned long long entries = stats[0], overlap = stats[1];
   return entries > 0 && overlap * 4 < entries;
 }
+
+// Tokens per chunk of the order's stable counting sort (order.hip).
+constexpr int kOrderChunk = 4096;
 
 // Workgroup L of a launch runs on XCD L % kXcds.
 constexpr int kXcds = 8;

@@ -16,11 +16,12 @@
 // order, otherwise the natural one.  Which order runs changes no output bit: every token's row is
 // computed by one wave from its own selection.
 //
-// Kernels, all on the caller's stream, one token per thread with its selection row in registers:
-// clear the counters; the adjacent-token share (on every 64th token); count block selections (per
-// (b, kvh), an LDS histogram per chunk of 1024 tokens flushed with atomics); key every token per
-// pass and histogram the keys; exclusive scan of the key counts per (b, kvh, pass); scatter the
-// tokens to their sorted positions.  When the share says natural, the last four exit at once.
+// Kernels, all on the caller's stream: clear the counters; the adjacent-token share (on every 64th
+// token); count block selections (per (b, kvh), an LDS histogram per 1024 tokens flushed with
+// atomics); key every token per pass and count the keys per chunk of kOrderChunk tokens; the
+// prefix of each key's counts over the chunks, then of the key totals; scatter the tokens to their
+// positions, a stable counting sort (ties in position order).  When the share says natural, all
+// but the first two exit at once.
 #include <algorithm>
 
 #include "kernels.h"
@@ -44,9 +45,7 @@ __device__ inline void load_row(const OrderArgs& a, int bh, int t, int (&r)[kOrd
 
 __global__ __launch_bounds__(256) void order_clear_kernel(OrderArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nh = (int64_t)a.bh * a.m1, nk = (int64_t)a.n_passes * a.bh * (a.m1 + 1);
-  if (i < nh) a.hist[i] = 0;
-  if (i < nk) a.keycnt[i] = 0;
+  if (i < (int64_t)a.bh * a.m1) a.hist[i] = 0;
   if (i < 2) a.stats[i] = 0ull;
 }
 
@@ -113,23 +112,26 @@ __global__ __launch_bounds__(kOrderThreads) void order_hist_kernel(OrderArgs a) 
 }
 
 // Key of every token in every pass: its smallest valid block j with j % n_passes == p that is not
-// hot, or m1 when the pass has none; stored, and counted per (b, kvh, pass) through an LDS
-// histogram of n_passes * (m1 + 1) counters.
+// hot, or m1 when the pass has none; stored, and counted per (pass, b, kvh, chunk of kOrderChunk
+// tokens) through an LDS histogram.  The chunk's counts go to the key-major matrix
+// keycnt[p][bh][key][chunk], every entry written.
 __global__ __launch_bounds__(kOrderThreads) void order_keys_kernel(OrderArgs a) {
   if (!order_sorted(a.stats)) return;
   extern __shared__ int lds_cnt[];
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
   const int nb = a.n_passes * (a.m1 + 1);
-  const int t = blockIdx.x * kOrderThreads + threadIdx.x;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) lds_cnt[i] = 0;
   __syncthreads();
-  if (t < a.n) {
-    const int32_t* hist = a.hist + (int64_t)bh * a.m1;
-    int r[kOrderMaxK];
-    load_row(a, bh, t, r);
+  const int32_t* hist = a.hist + (int64_t)bh * a.m1;
+  for (int r = 0; r < kOrderChunk / kOrderThreads; ++r) {
+    const int t = chunk * kOrderChunk + r * kOrderThreads + threadIdx.x;
+    if (t >= a.n) break;
+    int row[kOrderMaxK];
+    load_row(a, bh, t, row);
     int cold[kOrderMaxK];                   // the valid entries that are not hot, else m1
 #pragma unroll
-    for (int i = 0; i < kOrderMaxK; ++i) cold[i] = valid_entry(r[i], t) && hist[r[i]] <= a.hot_cut ? r[i] : a.m1;
+    for (int i = 0; i < kOrderMaxK; ++i)
+      cold[i] = valid_entry(row[i], t) && hist[row[i]] <= a.hot_cut ? row[i] : a.m1;
     for (int p = 0; p < a.n_passes; ++p) {
       int key = a.m1;
 #pragma unroll
@@ -142,15 +144,38 @@ __global__ __launch_bounds__(kOrderThreads) void order_keys_kernel(OrderArgs a) 
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += blockDim.x) {
     const int p = i / (a.m1 + 1), key = i % (a.m1 + 1);
-    if (lds_cnt[i]) atomicAdd(&a.keycnt[((int64_t)p * a.bh + bh) * (a.m1 + 1) + key], lds_cnt[i]);
+    a.keycnt[(((int64_t)p * a.bh + bh) * (a.m1 + 1) + key) * a.n_chunks + chunk] = lds_cnt[i];
   }
 }
 
-// Exclusive scan of one (pass, b, kvh)'s m1 + 1 key counts, in place: the counts become cursors.
-__global__ __launch_bounds__(1024) void order_scan_kernel(OrderArgs a) {
+// Per (pass, b, kvh) and key, one thread: the exclusive prefix of the key's counts over the chunks,
+// in place, and the key's total.
+__global__ __launch_bounds__(256) void order_prefix_kernel(OrderArgs a) {
+  if (!order_sorted(a.stats)) return;
+  const int64_t seg = blockIdx.y;
+  const int key = blockIdx.x * blockDim.x + threadIdx.x;
+  if (key > a.m1) return;
+  int32_t* cnt = a.keycnt + (seg * (a.m1 + 1) + key) * a.n_chunks;
+  int run = 0;
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < a.n_chunks ? cnt[c0 + i] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (c0 + i < a.n_chunks) cnt[c0 + i] = run;
+      run += v[i];
+    }
+  }
+  a.keytot[seg * (a.m1 + 1) + key] = run;
+}
+
+// Per (pass, b, kvh): exclusive scan of the m1 + 1 key totals, in place (the first position of each
+// key in the pass's order).
+__global__ __launch_bounds__(1024) void order_keyscan_kernel(OrderArgs a) {
   if (!order_sorted(a.stats)) return;
   __shared__ int wave_sum[1024 / 64];
-  int32_t* cnt = a.keycnt + (int64_t)blockIdx.x * (a.m1 + 1);
+  int32_t* cnt = a.keytot + (int64_t)blockIdx.x * (a.m1 + 1);
   const int nb = a.m1 + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x / 64;
   const int per = (nb + blockDim.x - 1) / blockDim.x;
@@ -182,27 +207,52 @@ __global__ __launch_bounds__(1024) void order_scan_kernel(OrderArgs a) {
   }
 }
 
-// Every token to its sorted position in each pass's order (positions within one key in any order),
-// a chunk of tokens per workgroup: a token's rank among the chunk's tokens with the same key comes
-// from an LDS counter, and one thread per key and chunk reserves the chunk's positions with one
-// global atomic, so popular keys do not serialise on the global cursor.
-__global__ __launch_bounds__(kOrderThreads) void order_scatter_kernel(OrderArgs a) {
+// Every token to its position in each pass's order: one wave per (chunk, b, kvh, pass) walks the
+// chunk's tokens in position order, 64 at a time.  A token's position is the first position of its
+// key, plus the chunk's offset within the key, plus the number of the chunk's earlier tokens with
+// the same key: those of earlier steps are counted in LDS, those of the same step by matching the
+// key bits across the wave with ballots.  Keys and bases are fetched 16 steps at a time.
+__global__ __launch_bounds__(64) void order_scatter_kernel(OrderArgs a) {
   if (!order_sorted(a.stats)) return;
-  extern __shared__ int lds_slot[];         // m1 + 1 counters, then bases
-  const int bh = blockIdx.y;
-  const int t = blockIdx.x * kOrderThreads + threadIdx.x;
-  const bool live = t < a.n;
-  for (int p = 0; p < a.n_passes; ++p) {
-    const int64_t base = (int64_t)p * a.bh + bh;
-    for (int i = threadIdx.x; i <= a.m1; i += blockDim.x) lds_slot[i] = 0;
-    __syncthreads();
-    const int key = live ? a.keys[base * a.n + t] : 0;
-    const int rank = live ? atomicAdd(&lds_slot[key], 1) : -1;
-    __syncthreads();
-    if (rank == 0) lds_slot[key] = atomicAdd(&a.keycnt[base * (a.m1 + 1) + key], lds_slot[key]);
-    __syncthreads();
-    if (live) a.order[base * a.n + lds_slot[key] + rank] = t;
-    __syncthreads();
+  extern __shared__ int lds_seen[];         // m1 + 1 counters
+  const int bh = blockIdx.y, chunk = blockIdx.x, p = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int key_bits = 32 - __builtin_clz((unsigned)a.m1);   // keys are 0 .. m1
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int64_t seg = (int64_t)p * a.bh + bh;
+  for (int i = lane; i <= a.m1; i += 64) lds_seen[i] = 0;
+  wave_lds_sync();
+  const int32_t* keys = a.keys + seg * a.n;
+  const int32_t* local = a.keycnt + seg * (int64_t)(a.m1 + 1) * a.n_chunks + chunk;
+  const int32_t* start = a.keytot + seg * (int64_t)(a.m1 + 1);
+  int32_t* order = a.order + seg * a.n;
+  const int t0 = chunk * kOrderChunk;
+  for (int s0 = 0; s0 < kOrderChunk / 64 && t0 + s0 * 64 < a.n; s0 += 16) {
+    int key[16], base[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + (s0 + i) * 64 + lane;
+      key[i] = t < a.n ? keys[t] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      base[i] = key[i] >= 0 ? start[key[i]] + local[(int64_t)key[i] * a.n_chunks] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + (s0 + i) * 64 + lane;
+      const bool live = key[i] >= 0;
+      uint64_t same = __ballot(live);
+      for (int b = 0; b < key_bits; ++b) {
+        const uint64_t ones = __ballot(live && ((key[i] >> b) & 1));
+        same &= ((key[i] >> b) & 1) ? ones : ~ones;
+      }
+      const int rank = __popcll(same & below), count = __popcll(same);
+      const int seen = live ? lds_seen[key[i]] : 0;
+      if (live) order[base[i] + seen + rank] = t;
+      wave_lds_sync();
+      if (live && rank == count - 1) lds_seen[key[i]] = seen + count;
+      wave_lds_sync();
+    }
   }
 }
 
@@ -213,29 +263,31 @@ size_t order_keys_lds_bytes(int m1, int n_passes) { return (size_t)n_passes * (m
 
 hipError_t launch_order(const OrderArgs& a, hipStream_t s) {
   if (a.top_k > kOrderMaxK) return hipErrorInvalidValue;
-  const int64_t clear = std::max<int64_t>((int64_t)a.bh * a.m1, (int64_t)a.n_passes * a.bh * (a.m1 + 1));
+  const int64_t clear = std::max<int64_t>((int64_t)a.bh * a.m1, 2);
   hipLaunchKernelGGL(order_clear_kernel, dim3((unsigned)((clear + 255) / 256)), dim3(256), 0, s, a);
   hipError_t e = launched(s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(order_share_kernel, dim3(ceil_div(ceil_div(a.n, kOrderSample), 8), a.bh), dim3(256), 0, s, a);
   if ((e = launched(s)) != hipSuccess) return e;
-  const dim3 chunks(ceil_div(a.n, kOrderThreads), a.bh);
   const size_t lds_hist = order_hist_lds_bytes(a.m1), lds_keys = order_keys_lds_bytes(a.m1, a.n_passes),
-               lds_slots = order_hist_lds_bytes(a.m1 + 1);
+               lds_seen = order_hist_lds_bytes(a.m1 + 1);
   const void* kernels[3] = {(const void*)order_hist_kernel, (const void*)order_keys_kernel,
                             (const void*)order_scatter_kernel};
-  const size_t lds[3] = {lds_hist, lds_keys, lds_slots};
+  const size_t lds[3] = {lds_hist, lds_keys, lds_seen};
   for (int i = 0; i < 3; ++i)
     if (lds[i] > 64 * 1024 &&
         (e = hipFuncSetAttribute(kernels[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i])) != hipSuccess)
       return e;
-  hipLaunchKernelGGL(order_hist_kernel, chunks, dim3(kOrderThreads), lds_hist, s, a);
+  hipLaunchKernelGGL(order_hist_kernel, dim3(ceil_div(a.n, kOrderThreads), a.bh), dim3(kOrderThreads), lds_hist, s, a);
   if ((e = launched(s)) != hipSuccess) return e;
+  const dim3 chunks(a.n_chunks, a.bh);
   hipLaunchKernelGGL(order_keys_kernel, chunks, dim3(kOrderThreads), lds_keys, s, a);
   if ((e = launched(s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(order_scan_kernel, dim3(a.n_passes * a.bh), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(order_prefix_kernel, dim3(ceil_div(a.m1 + 1, 256), a.n_passes * a.bh), dim3(256), 0, s, a);
   if ((e = launched(s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(order_scatter_kernel, chunks, dim3(kOrderThreads), lds_slots, s, a);
+  hipLaunchKernelGGL(order_keyscan_kernel, dim3(a.n_passes * a.bh), dim3(1024), 0, s, a);
+  if ((e = launched(s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(order_scatter_kernel, dim3(a.n_chunks, a.bh, a.n_passes), dim3(64), lds_seen, s, a);
   return launched(s);
 }
 

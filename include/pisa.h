@@ -113,10 +113,10 @@ int pisa_last_hip_error(void);
  * call.  Kernels per call: build_pyramid 1 or 2 (leaves, then the top levels
  * above 8 leaves); select_blocks 5 or 6 (split summaries for bf16 inputs,
  * routing, clustering, packing of K for bf16 inputs, leaf LSE, top-K);
- * sparse_attn_fwd with bf16 inputs 1 + passes, or 7 + passes up to 16384 leaf
- * blocks (packing of K and V; the six kernels of the passes' token order:
- * clear, adjacent-token share, block counts, keys, scan, scatter; then one
- * launch per pass), fp32 inputs 1; decode_step 1;
+ * sparse_attn_fwd with bf16 inputs 1 + passes, or 8 + passes up to 16384 leaf
+ * blocks (packing of K and V; the seven kernels of the passes' token order:
+ * clear, adjacent-token share, block counts, keys, per-key prefix over chunks,
+ * key starts, scatter; then one launch per pass), fp32 inputs 1; decode_step 1;
  * select_flat 3.  count = 0 clears the list.  Returns PISA_ERR_INVALID_ARG
  * for count < 0 or a null array or handle. */
 pisa_status pisa_stage_events(void* const* events, int32_t count);
@@ -203,9 +203,10 @@ pisa_status pisa_select_flat(const pisa_cfg* cfg, pisa_tensor q, const float* py
  * call (even block ids, then odd ones; the output rows hold the partial sums
  * between them), then, up to 16384 leaf blocks (N <= 1048576), the arrays that
  * order each pass's tokens: B * H_kv * ceil(N / 64) block counts, 2 * B * H_kv *
- * (ceil(N / 64) + 1) key counts, two 64-bit statistics, 2 * B * H_kv * N token
- * keys and 2 * B * H_kv * N token positions (4 bytes each, every array rounded
- * up to 256); fp32 inputs need none (0). */
+ * (ceil(N / 64) + 1) * ceil(N / 4096) key counts per chunk of 4096 tokens,
+ * 2 * B * H_kv * (ceil(N / 64) + 1) key totals, two 64-bit statistics,
+ * 2 * B * H_kv * N token keys and 2 * B * H_kv * N token positions (4 bytes
+ * each, every array rounded up to 256); fp32 inputs need none (0). */
 size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
 
 /*
@@ -232,8 +233,9 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  * With bf16 inputs the passes visit tokens either in position order or, when
  * the selections' blocks are listed by the previous token less than a quarter
  * of the time (measured on the device, per call), sorted by each token's
- * smallest block of the pass selected at most 4 * 64 * K times, in eight
- * contiguous slices, one per XCD, so tokens sharing such a block meet in one L2.
+ * smallest block of the pass selected at most 4 * 64 * K times (ties in
+ * position order), in eight contiguous slices, one per XCD, so tokens sharing
+ * such a block meet in one L2.
  * Either way every row is computed from its own selection alone: the outputs
  * are the same bit for bit.
  */

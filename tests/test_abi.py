@@ -111,11 +111,12 @@ def test_invalid_tensors_are_rejected_before_launch(lib):
                                     None, ctypes.c_void_p(4096), 1 << 30, None) == 1
     # bf16 attention needs its workspace: packed K and V blocks, the (m, l) pair of every
     # (token, query head) carried between the two passes of a float32-output call, then the token
-    # order of the passes (block counts, key counts, two 64-bit statistics, the tokens' keys and
-    # their positions, two passes each), each array rounded up to 256 bytes
+    # order of the passes (block counts, key counts per chunk of 4096 tokens and key totals, two
+    # 64-bit statistics, the tokens' keys and their positions, two passes each), each array rounded
+    # up to 256 bytes
     up = lambda x: -(-x // 256) * 256
     m1 = 4096 // 64
-    want = (2 * 4096 * 128 * 2 + 16 * 4096 * 2 * 4 + up(m1 * 4) + up(2 * (m1 + 1) * 4) + 256
+    want = (2 * 4096 * 128 * 2 + 16 * 4096 * 2 * 4 + up(m1 * 4) + 2 * up(2 * (m1 + 1) * 4) + 256
             + 2 * up(2 * 4096 * 4))
     assert lib.pisa_attn_workspace_bytes(ctypes.byref(cfg)) == want
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(cfg), good, good, good, ctypes.c_void_p(4096), good, 0,
