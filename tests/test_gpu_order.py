@@ -4,9 +4,10 @@ checked against a plain host computation of the same rule:
 * the adjacent-token statistic: over every 64th token t (t = 1, 65, ...), the valid entries of row t
   and how many of them row t - 1 also lists among its valid entries;
 * the choice: sorted order when fewer than a quarter of those entries are shared;
-* with the sorted order, for each pass p: every token's key is its smallest valid block j with
-  j % passes == p that was selected at most 4 * 64 * K times in the whole call (else ceil(N / 64)),
-  and the pass's order is the tokens sorted by key with ties in position order;
+* with the sorted order, for each pass p (two for a float32 output, one for bfloat16): every token's
+  key is its smallest valid block j with j % passes == p that was selected at most 4 * 64 * K times
+  in the whole call (else ceil(N / 64)), and the pass's order is the tokens sorted by key with ties
+  in position order;
 * the attention output is the same bit for bit whichever order runs (the natural order is forced
   by a selection whose rows repeat the previous row's blocks), and matches the oracle.
 
@@ -50,7 +51,7 @@ def layout(B, N, Hq, Hkv, d):
     return dict(m1=m1, bh=bh, hist=hist, stats=stats, keys=keys, order=order, total=total)
 
 
-def host_rule(sel: np.ndarray, K: int):
+def host_rule(sel: np.ndarray, K: int, passes: int = PASSES):
     """sel [bh, N, K] -> (entries, overlap, sorted?, keys [passes, bh, N])."""
     bh, N, _ = sel.shape
     m1 = -(-N // 64)
@@ -68,15 +69,15 @@ def host_rule(sel: np.ndarray, K: int):
     hist = np.zeros((bh, m1), np.int64)
     for b in range(bh):
         np.add.at(hist[b], sel[b][valid[b]], 1)
-    keys = np.full((PASSES, bh, N), m1, np.int64)
+    keys = np.full((passes, bh, N), m1, np.int64)
     for b in range(bh):
         cold = valid[b] & (hist[b][np.clip(sel[b], 0, m1 - 1)] <= 4 * 64 * K)
-        for p in range(PASSES):
-            keys[p, b] = np.where(cold & (sel[b] % PASSES == p), sel[b], m1).min(-1)
+        for p in range(passes):
+            keys[p, b] = np.where(cold & (sel[b] % passes == p), sel[b], m1).min(-1)
     return entries, overlap, is_sorted, keys
 
 
-def run(w: W.Workload, sel: np.ndarray):
+def run(w: W.Workload, sel: np.ndarray, out_dtype=torch.float32):
     q, k, v = W.prefill_inputs(w, bits=True)
     qd, kd, vd = H.to_device(q, w), H.to_device(k, w), H.to_device(v, w)
     B, N, Hq, d = qd.shape
@@ -85,28 +86,30 @@ def run(w: W.Workload, sel: np.ndarray):
     assert binding.attn_workspace_bytes(cfg) == lay["total"]
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device=H.DEV)
     seld = torch.from_numpy(sel.astype(np.int32).reshape(B, w.n_kv_heads, N, w.top_k)).to(H.DEV)
-    o = binding.sparse_attn_fwd(qd, kd, vd, seld, out_dtype=torch.float32, workspace=ws)
+    o = binding.sparse_attn_fwd(qd, kd, vd, seld, out_dtype=out_dtype, workspace=ws)
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     stats = raw[lay["stats"]:lay["stats"] + 16].view(np.uint64)
     bhN = lay["bh"] * N
     keys = raw[lay["keys"]:lay["keys"] + PASSES * bhN * 4].view(np.int32).reshape(PASSES, lay["bh"], N)
     order = raw[lay["order"]:lay["order"] + PASSES * bhN * 4].view(np.int32).reshape(PASSES, lay["bh"], N)
-    return (q, k, v), o.cpu().numpy(), stats, keys, order
+    return (q, k, v), o.float().cpu().numpy(), stats, keys, order
 
 
-def check_case(w: W.Workload, sel: np.ndarray, want_sorted: bool, label: str):
+def check_case(w: W.Workload, sel: np.ndarray, want_sorted: bool, label: str, out_dtype=torch.float32):
+    """A float32 output runs two passes (even, then odd block ids), a bfloat16 output one."""
     bh = w.batch * w.n_kv_heads
+    passes = PASSES if out_dtype == torch.float32 else 1
     sel3 = sel.reshape(bh, w.seq_len, w.top_k)
-    entries, overlap, is_sorted, keys_want = host_rule(sel3, w.top_k)
+    entries, overlap, is_sorted, keys_want = host_rule(sel3, w.top_k, passes)
     assert is_sorted == want_sorted, (label, entries, overlap)
-    (q, k, v), o, stats, keys, order = run(w, sel)
+    (q, k, v), o, stats, keys, order = run(w, sel, out_dtype)
     H.log(f"[{label}] entries {int(stats[0])} overlap {int(stats[1])} (host {entries} / {overlap}), "
           f"{'sorted' if is_sorted else 'natural'} order")
     assert int(stats[0]) == entries and int(stats[1]) == overlap, (label, stats, entries, overlap)
     if is_sorted:
-        np.testing.assert_array_equal(keys, keys_want)
-        for p in range(PASSES):
+        np.testing.assert_array_equal(keys[:passes], keys_want)
+        for p in range(passes):
             for b in range(bh):
                 want = np.lexsort((np.arange(w.seq_len), keys_want[p, b]))
                 np.testing.assert_array_equal(order[p, b], want, err_msg=f"{label} pass {p} unit {b}")
@@ -119,8 +122,12 @@ def check_case(w: W.Workload, sel: np.ndarray, want_sorted: bool, label: str):
                                           H.host_values(k[b, :, kvh]).astype(np.float64),
                                           H.host_values(v[b, :, kvh]).astype(np.float64),
                                           sel[b, kvh], np.arange(w.seq_len))
-            ma, rl = H.attn_errors(o[b][:, kvh * G:(kvh + 1) * G], want)
-            assert ma <= tol_abs and rl <= tol_rel, (label, b, kvh, ma, rl)
+            got = o[b][:, kvh * G:(kvh + 1) * G]
+            if out_dtype == torch.float32:
+                ma, rl = H.attn_errors(got, want)
+                assert ma <= tol_abs and rl <= tol_rel, (label, b, kvh, ma, rl)
+            else:
+                H.assert_bf16_output(got, want, label)
     return o
 
 
@@ -148,6 +155,8 @@ def test_order_statistics_keys_and_permutation():
         new = np.concatenate([prev[..., 1:], np.full(prev.shape[:-1] + (1,), t // 64)], axis=-1)
         rep[:, :, t] = np.where((prev >= 0).all(-1, keepdims=True), new, rand[:, :, t])
     o_natural = check_case(w, rep, False, "repeated rows")
+    # one pass (bfloat16 output): the keys and the order of the single pass
+    check_case(w, rand, True, "random rows, one pass", out_dtype=torch.bfloat16)
     # tokens whose rows are equal in both selections: the same output bits in either order
     same = np.all(rand == rep, axis=-1)                       # [B, Hkv, N]
     for b in range(w.batch):
