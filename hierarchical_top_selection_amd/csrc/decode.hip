@@ -64,7 +64,7 @@ __device__ inline void decode_update_unit(const DecodeArgs& a, int bh, int c) {
 //  * routing, level by level from the root: the candidates' children are scored 16 at a time as the
 //    rows of an S^T = (children) Q^T MFMA tile (fp32 summaries, v_mfma_f32_16x16x4_f32), one tile per
 //    wave; a candidate's two children sit in the same lane, so its per-head LSE is in-lane and the
-//    head sum a DPP row reduction; wave 0 ranks (score descending, index ascending) and expands;
+//    head sum a DPP row reduction; wave 0 keeps K by (score descending, index ascending) and expands;
 //  * leaf scoring: one candidate leaf per wave, S^T over its 64 raw keys on the input type's MFMA;
 //    the logits (base-2 units) are staged in LDS and reused by the attention, so the selected keys
 //    are read from HBM once; every level scores with the configured candidate score (LSE, or the
@@ -76,52 +76,51 @@ constexpr int kDecodeWaves = 8;
 
 // LDS carve-up of the fused kernel (4-byte words).
 struct DecodeLds {
-  int zl, part, us, hstat, prank, ints;
+  int zl, part, us, hstat, ints;
   size_t bytes;
   __host__ __device__ DecodeLds(int G, int width, int D) {
     zl = 0;                                   // width * 64 * G staged leaf logits, then probabilities
     part = zl + width * kLeaf * G;            // kDecodeWaves * G * D partial outputs
     us = part + kDecodeWaves * G * D;         // 64 candidate scores
     hstat = us + 64;                          // per-head max and 1 / sum
-    prank = hstat + 2 * G;                    // kDecodeWaves * 64 partial ranks
-    ints = prank + kDecodeWaves * 64;         // cand[64], keep[64], selv[64], sels[64], misc[4]
-    bytes = (size_t)(ints + 4 * 64 + 4) * 4;
+    ints = hstat + 2 * G;                     // cand[64], selv[64], sels[64], misc[4]
+    bytes = (size_t)(ints + 3 * 64 + 4) * 4;
   }
 };
 
-// Order-preserving key of a candidate for the ranking (score descending, index ascending): the
-// score's bits made order-preserving (-0 as +0) above the complemented index; empty slots are 0.
-__device__ inline uint64_t rank_key(float u, int c) {
-  const uint32_t ub = __builtin_bit_cast(uint32_t, u + 0.f);
-  const uint32_t hi = c >= 0 ? ((ub & 0x80000000u) ? ~ub : (ub | 0x80000000u)) : 0u;
-  const uint32_t lo = c >= 0 ? 0xffffffffu - (uint32_t)c : 0u;
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Ranking shared by the waves: wave w counts, for every slot (lane), how many of the slots
-// [8 w, 8 w + 8) beat it; the slots' scores and indices are read from LDS (broadcast reads).
-__device__ inline void decode_rank_partial(const int* cand, const float* us, int nslots, int* prank, int wave,
-                                           int lane) {
-  const uint64_t mine = lane < nslots ? rank_key(us[lane], cand[lane]) : 0ull;
-  int cnt = 0;
+// Keep flag of lane i's candidate among the wave's K best by (score descending, index ascending).
+// khi is the candidate's score bits made order-preserving (0 for an empty lane, above 0 for every
+// valid one), and the valid lanes hold ascending indices, so among equal scores the lower lane is
+// the lower index.  Needs more than K valid lanes.  A bitwise search from the top bit finds the
+// K-th largest khi as the largest threshold that at least K lanes reach; every lane above it is
+// kept, and the lowest lanes equal to it fill the places that remain.
+__device__ inline bool keep_top_k(uint32_t khi, int k) {
+  uint32_t thr = 0;
 #pragma unroll
-  for (int i = 0; i < 64 / kDecodeWaves; ++i) {
-    const int j = wave * (64 / kDecodeWaves) + i;
-    if (j < nslots) cnt += (int)(rank_key(us[j], cand[j]) > mine);
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = thr | (1u << bit);
+    if (__popcll(__ballot(khi >= trial)) >= k) thr = trial;
   }
-  prank[wave * 64 + lane] = cnt;
+  const uint64_t ties = __ballot(khi == thr);
+  const int need = k - __popcll(__ballot(khi > thr));
+  const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ties >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)ties, 0u));
+  return khi > thr || (khi == thr && before < need);
 }
 
-// Wave 0: keep candidates by exact rank (u descending, index ascending), the sum of the waves'
-// partial counts, or, when at most K are valid, all of them.  Returns this lane's keep flag
-// (lane i = slot i).
-__device__ inline bool decode_keep(const int* cand, const int* prank, int nslots, int nvalid, int K, int lane) {
-  const int ci = lane < nslots ? cand[lane] : -1;
-  if (nvalid <= K) return ci >= 0;
-  int rank = 0;
-#pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) rank += prank[w * 64 + lane];
-  return ci >= 0 && rank < K;
+// Order-preserving bits of a score (-0 as +0) for keep_top_k; 0 for an empty lane.
+__device__ inline uint32_t score_key(float u, bool valid) {
+  const uint32_t ub = __builtin_bit_cast(uint32_t, u + 0.f);
+  return valid ? ((ub & 0x80000000u) ? ~ub : (ub | 0x80000000u)) : 0u;
+}
+
+// Wave 0: keep flag of slot `lane` (candidate ci): when more than K are valid, the K best by
+// (score descending, index ascending), else every valid one.  The valid slots are the lowest ones
+// and hold ascending indices (each expansion keeps the parents' slot order and only the last
+// parent can lose its second child), as keep_top_k needs.
+__device__ inline bool decode_keep(int ci, const float* us, int nvalid, int K, int lane) {
+  const bool best = nvalid > K ? keep_top_k(score_key(us[lane], ci >= 0), K) : true;   // uniform branch
+  return ci >= 0 && best;
 }
 
 template <typename T, typename TO, int D, int G>
@@ -136,11 +135,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float* us = smem + L.us;
   float* hstat = smem + L.hstat;
   int* cand = reinterpret_cast<int*>(smem + L.ints);
-  int* keep = cand + 64;
-  int* selv = keep + 64;               // selected leaf ids, ascending
+  int* selv = cand + 64;               // selected leaf ids, ascending
   int* sels = selv + 64;               // their candidate slots
   int* misc = sels + 64;               // [0] slots, [1] valid, [2] selected
-  int* prank = reinterpret_cast<int*>(smem + L.prank);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -188,13 +185,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       }
     }
     __syncthreads();
-    if (nvalid > K) {
-      decode_rank_partial(cand, us, nslots, prank, wave, lane);
-      __syncthreads();
-    }
     if (wave == 0) {
-      const bool kp = decode_keep(cand, prank, nslots, nvalid, K, lane);
       const int ci = lane < nslots ? cand[lane] : -1;
+      const bool kp = decode_keep(ci, us, nvalid, K, lane);
       const uint64_t kept = __ballot(kp);
       const int m = __popcll(kept);
       const int p = lane >> 1;
@@ -278,13 +271,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if (lane == 15) us[slot] = u;
   }
   __syncthreads();
-  if (nvalid > K) {
-    decode_rank_partial(cand, us, nslots, prank, wave, lane);
-    __syncthreads();
-  }
   if (wave == 0) {
-    const bool kp = decode_keep(cand, prank, nslots, nvalid, K, lane);
-    const int c = kp ? cand[lane] : 0x7fffffff;
+    const int ci = lane < nslots ? cand[lane] : -1;
+    const bool kp = decode_keep(ci, us, nvalid, K, lane);
+    const int c = kp ? ci : 0x7fffffff;
     int pos = 0;                                        // ascending leaf order among the kept
     for (int j = 0; j < 64; ++j) pos += __builtin_amdgcn_readlane(c, j) < c;
     if (kp) { selv[pos] = c; sels[pos] = lane; }
