@@ -2,6 +2,7 @@
 // geometry, workspace carving and kernel launch order.  Nothing here allocates
 // or synchronises; every call enqueues on the caller's stream.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -228,8 +229,20 @@ bool attn_has_order(const pisa_cfg* c) { return attn_layout(c).order != 0; }
 
 namespace pisa {
 
+// Debug mode: with PISA_SYNC_LAUNCHES set to a value other than "0" in the environment when the
+// library first launches, every launch waits for its stream, so a kernel's fault or error is
+// reported by the entry point and the kernel that caused it (not by a later call).  Read once.
+static bool sync_launches() {
+  static const bool on = [] {
+    const char* v = getenv("PISA_SYNC_LAUNCHES");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
 hipError_t launched(hipStream_t s) {
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sync_launches()) e = hipStreamSynchronize(s);
   if (e != hipSuccess || g_stage_left <= 0) return e;
   e = hipEventRecord(static_cast<hipEvent_t>(*g_stage_events), s);
   ++g_stage_events;
@@ -254,7 +267,7 @@ pisa_status pisa_stage_events(void* const* events, int32_t count) {
 
 int pisa_abi_version(void) { return PISA_ABI_VERSION; }
 
-const char* pisa_status_string(pisa_status s) {
+const char* pisa_status_string(int32_t s) {
   switch (s) {
     case PISA_OK: return "ok";
     case PISA_ERR_INVALID_ARG: return "invalid argument";
@@ -414,7 +427,7 @@ namespace {
 
 // Forward attention with the workspace the caller (or the fixed device array) provides.
 pisa_status attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v, const int32_t* sel,
-                     pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse, void* ws, size_t ws_bytes,
+                     pisa_tensor_mut o, int32_t o_dtype, float* row_lse, void* ws, size_t ws_bytes,
                      void* stream) {
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;
@@ -506,14 +519,14 @@ void* scratch_on_current_device() {
 extern "C" {
 
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 const int32_t* sel, pisa_tensor_mut o, int32_t o_dtype, float* row_lse,
                                  void* ws, size_t ws_bytes, void* stream) {
   StageScope stages;
   return attn_fwd(cfg, q, k, v, sel, o, o_dtype, row_lse, ws, ws_bytes, stream);
 }
 
 pisa_status pisa_sparse_attn_fwd_noalloc(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                         const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype,
+                                         const int32_t* sel, pisa_tensor_mut o, int32_t o_dtype,
                                          float* row_lse, void* stream) {
   StageScope stages;
   pisa_status st = check_cfg(cfg);
@@ -531,7 +544,7 @@ size_t pisa_attn_bwd_workspace_bytes(const pisa_cfg* cfg) {
 }
 
 pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, pisa_dtype grad_dtype,
+                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, int32_t grad_dtype,
                                  const float* row_lse, pisa_tensor_mut dq, pisa_tensor_mut dk, pisa_tensor_mut dv,
                                  void* ws, size_t ws_bytes, void* stream) {
   StageScope stages;
@@ -582,7 +595,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
 
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
                              pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache, float* pyr,
-                             int32_t* sel_out, pisa_tensor_mut o, pisa_dtype o_dtype, void* stream) {
+                             int32_t* sel_out, pisa_tensor_mut o, int32_t o_dtype, void* stream) {
   StageScope stages;
   pisa_status st = check_cfg(cfg);
   if (st != PISA_OK) return st;

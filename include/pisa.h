@@ -35,6 +35,11 @@
  *    pisa_status means nothing was launched, except PISA_ERR_HIP, which means a
  *    launch failed (pisa_last_hip_error() then returns the hipError_t value of
  *    the calling thread's last failure).  No C++ exception crosses the ABI.
+ *  - Debug mode: when the environment variable PISA_SYNC_LAUNCHES holds a value
+ *    other than "0" at the library's first launch, every launch waits for its
+ *    stream (hipStreamSynchronize), so an asynchronous fault or error of a kernel
+ *    is returned as PISA_ERR_HIP by the entry point that launched it.  This is the
+ *    one exception to "never synchronises"; do not use it under stream capture.
  *  - Thread safety: no global mutable state besides the thread-local error code,
  *    the thread-local stage events of pisa_stage_events and the per-device
  *    address of the fixed array behind pisa_sparse_attn_fwd_noalloc (set once,
@@ -61,6 +66,9 @@ typedef enum {
 } pisa_status;
 
 typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+/* Fields and arguments that take a pisa_dtype or pisa_score value are declared int32_t, so any
+ * value a caller passes is representable and an unknown one is rejected as
+ * PISA_ERR_INVALID_ARG (an enum type cannot hold a value outside its enumerators in C++). */
 
 /*
  * Problem description.  Supported envelope: block == 64 (C), fanout == 2 (g),
@@ -87,9 +95,9 @@ typedef struct {
   int32_t block;        /* C, leaf block size: must be 64 */
   int32_t fanout;       /* g, children per node above the leaves: must be 2 */
   int32_t top_k;        /* K, leaf blocks kept per (token, KV head) */
-  pisa_dtype dtype;     /* element type of Q, K, V, O and the KV caches */
+  int32_t dtype;        /* a pisa_dtype: element type of Q, K, V, O and the KV caches */
   float scale;          /* logit scale; <= 0 means 1/sqrt(head_dim) */
-  pisa_score score;     /* candidate score at every level (routing, leaves, decode) */
+  int32_t score;        /* a pisa_score: candidate score at every level (routing, leaves, decode) */
 } pisa_cfg;
 
 typedef struct { const void* ptr; int64_t stride_b, stride_t, stride_h; } pisa_tensor;
@@ -99,7 +107,7 @@ typedef struct { void* ptr; int64_t stride_b, stride_t, stride_h; } pisa_tensor_
 int pisa_abi_version(void);
 
 /* Static description of a status code. */
-const char* pisa_status_string(pisa_status status);
+const char* pisa_status_string(int32_t status);
 
 /* hipError_t of the calling thread's last failed launch (0 if none). */
 int pisa_last_hip_error(void);
@@ -240,7 +248,7 @@ size_t pisa_attn_workspace_bytes(const pisa_cfg* cfg);
  * are the same bit for bit.
  */
 pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype, float* row_lse,
+                                 const int32_t* sel, pisa_tensor_mut o, int32_t o_dtype, float* row_lse,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Size of the device array behind pisa_sparse_attn_fwd_noalloc (one per GPU). */
@@ -263,7 +271,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
  * caller.
  */
 pisa_status pisa_sparse_attn_fwd_noalloc(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                         const int32_t* sel, pisa_tensor_mut o, pisa_dtype o_dtype,
+                                         const int32_t* sel, pisa_tensor_mut o, int32_t o_dtype,
                                          float* row_lse, void* stream);
 
 /* Workspace bytes needed by pisa_sparse_attn_bwd for cfg (0 for an unsupported
@@ -303,7 +311,7 @@ size_t pisa_attn_bwd_workspace_bytes(const pisa_cfg* cfg);
  * when B * H_kv * N * K exceeds 2^31 - 1.
  */
 pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, pisa_tensor v,
-                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, pisa_dtype grad_dtype,
+                                 const int32_t* sel, pisa_tensor o, pisa_tensor dout, int32_t grad_dtype,
                                  const float* row_lse, pisa_tensor_mut dq, pisa_tensor_mut dk, pisa_tensor_mut dv,
                                  void* ws, size_t ws_bytes, void* stream);
 
@@ -330,7 +338,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor
  */
 pisa_status pisa_decode_step(const pisa_cfg* cfg, int32_t n_ctx, pisa_tensor q, pisa_tensor k_new,
                              pisa_tensor v_new, pisa_tensor_mut k_cache, pisa_tensor_mut v_cache,
-                             float* pyr, int32_t* sel_out, pisa_tensor_mut o, pisa_dtype o_dtype,
+                             float* pyr, int32_t* sel_out, pisa_tensor_mut o, int32_t o_dtype,
                              void* stream);
 
 #ifdef __cplusplus

@@ -46,6 +46,8 @@ def test_stage_events_validation(lib):
 def test_status_strings(lib):
     assert lib.pisa_status_string(0).decode() == "ok"
     assert "unsupported" in lib.pisa_status_string(2).decode()
+    assert lib.pisa_status_string(99).decode() == "unknown status"
+    assert lib.pisa_status_string(-1).decode() == "unknown status"
 
 
 @pytest.mark.parametrize("cap", [1, 63, 64, 65, 1024, 4096, 131072, 131328, 262144])
@@ -75,7 +77,8 @@ def test_workspace_and_pyramid_bytes(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, 2), ("top_k", 33, 2), ("top_k", 0, 1), ("n_kv_heads", 5, 1), ("n_q_heads", 24, 2),
-    ("block", 32, 2), ("fanout", 4, 2), ("seq_len", 0, 1), ("batch", 0, 1), ("dtype", 7, 1),
+    ("block", 32, 2), ("fanout", 4, 2), ("seq_len", 0, 1), ("batch", 0, 1), ("dtype", 7, 1), ("dtype", -1, 1),
+    ("score", 3, 1), ("score", -5, 1),
 ])
 def test_invalid_configs_are_rejected_before_launch(lib, field, value, status):
     cfg = _cfg()
