@@ -221,6 +221,32 @@ __device__ inline float pair_score(float y0, float y1, bool ok0, bool ok1, int m
   return mode == 2 ? mean + 0.5f * h * h : mean;
 }
 
+// Keep flag of lane i's candidate among the wave's K best by (score descending, index ascending).
+// khi is the candidate's score bits made order-preserving (0 for an empty lane, above 0 for every
+// valid one), and the valid lanes hold ascending indices, so among equal scores the lower lane is
+// the lower index.  Needs more than K valid lanes.  A bitwise search from the top bit finds the
+// K-th largest khi as the largest threshold that at least K lanes reach; every lane above it is
+// kept, and the lowest lanes equal to it fill the places that remain.
+__device__ inline bool keep_top_k(uint32_t khi, int k) {
+  uint32_t thr = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = thr | (1u << bit);
+    if (__popcll(__ballot(khi >= trial)) >= k) thr = trial;
+  }
+  const uint64_t ties = __ballot(khi == thr);
+  const int need = k - __popcll(__ballot(khi > thr));
+  const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ties >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)ties, 0u));
+  return khi > thr || (khi == thr && before < need);
+}
+
+// Order-preserving bits of a score (-0 as +0) for keep_top_k; 0 for an empty lane.
+__device__ inline uint32_t score_key(float u, bool valid) {
+  const uint32_t ub = __builtin_bit_cast(uint32_t, u + 0.f);
+  return valid ? ((ub & 0x80000000u) ? ~ub : (ub | 0x80000000u)) : 0u;
+}
+
 // Index of the p-th set bit (p counted from 0) of a non-empty 64-bit mask.
 __device__ inline int nth_set_bit(uint64_t mask, int p) {
   int pos = 0;
