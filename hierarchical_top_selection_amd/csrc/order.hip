@@ -229,14 +229,20 @@ __global__ __launch_bounds__(64) void order_scatter_kernel(OrderArgs a) {
   const int t0 = chunk * kOrderChunk;
   for (int s0 = 0; s0 < kOrderChunk / 64 && t0 + s0 * 64 < a.n; s0 += 16) {
     int key[16], base[16];
+    // unconditional loads from clamped indices, the values selected afterwards: loads under a
+    // branch make the compiler wait for every load in flight where the paths merge
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = t0 + (s0 + i) * 64 + lane;
-      key[i] = t < a.n ? keys[t] : -1;
+      const int k = keys[min(t, a.n - 1)];
+      key[i] = t < a.n ? k : -1;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      base[i] = key[i] >= 0 ? start[key[i]] + local[(int64_t)key[i] * a.n_chunks] : 0;
+    for (int i = 0; i < 16; ++i) {
+      const int kk = max(key[i], 0);
+      const int b0 = start[kk] + local[(int64_t)kk * a.n_chunks];
+      base[i] = key[i] >= 0 ? b0 : 0;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = t0 + (s0 + i) * 64 + lane;
