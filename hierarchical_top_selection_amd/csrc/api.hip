@@ -110,7 +110,7 @@ pisa_status hip_status(hipError_t e) {
 }
 
 struct SelectWorkspace {
-  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, kpack, qpack, total;
+  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, lonorm, kpack, qpack, total;
   int n_windows, item_cap;
 };
 
@@ -135,10 +135,12 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   // bf16 inputs: split summaries for routing (4 bytes per pyramid element), packed K
   // blocks and packed query groups for the leaf scores
   const bool bf16 = c->dtype == PISA_BF16;
-  const size_t split_bytes = bf16 ? (size_t)bh * split_pairs(make_levels(c->seq_len, c->seq_len), nullptr) * c->head_dim * 8 : 0;
+  const int64_t split_blocks = bf16 ? bh * split_pairs(make_levels(c->seq_len, c->seq_len), nullptr) : 0;
+  const size_t split_bytes = (size_t)split_blocks * c->head_dim * 8;
   const size_t kpack_bytes = bf16 ? (size_t)bh * m1 * pisa::kLeaf * c->head_dim * 2 : 0;
   const size_t qpack_bytes = bf16 ? (size_t)bh * c->seq_len * c->n_q_heads / c->n_kv_heads * c->head_dim * 2 : 0;
-  w.kpack = align256(w.split + split_bytes);
+  w.lonorm = align256(w.split + split_bytes);         // two floats per split block
+  w.kpack = align256(w.lonorm + (size_t)split_blocks * 8);
   w.qpack = align256(w.kpack + kpack_bytes);
   w.total = align256(w.qpack + qpack_bytes);
   return w;
@@ -228,6 +230,17 @@ bool attn_has_order(const pisa_cfg* c) { return attn_layout(c).order != 0; }
 }  // namespace
 
 namespace pisa {
+
+// PISA_ROUTE_EXACT set to a value other than "0" in the environment at the first selection call:
+// bf16 LSE routing scores every candidate from the full split rows (route_kernel) instead of
+// pre-filtering with the high parts; the selections are the same either way.  Read once.
+static bool route_exact() {
+  static const bool on = [] {
+    const char* v = getenv("PISA_ROUTE_EXACT");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
 
 // Debug mode: with PISA_SYNC_LAUNCHES set to a value other than "0" in the environment when the
 // library first launches, every launch waits for its stream, so a kernel's fault or error is
@@ -343,6 +356,8 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16; r.score = cfg->score;
   r.lv = make_levels(N, N);
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
+  r.lonorm = bf16 ? reinterpret_cast<float*>(base + w.lonorm) : nullptr;
+  r.prefilter = bf16 && cfg->score == PISA_SCORE_LSE && !pisa::route_exact();
   r.pairs = split_pairs(r.lv, r.pair_off);
   pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
   pisa::bf16x8* qpack = reinterpret_cast<pisa::bf16x8*>(base + w.qpack);

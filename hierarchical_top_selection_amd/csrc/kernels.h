@@ -28,6 +28,9 @@ struct RouteArgs {
   // (per b * Hkv: `pairs` blocks).  Line (plane, s), plane 0 = high / 1 = remainder, s < d / 32,
   // is 128 bytes: elements [32 s, 32 s + 32) of node 2p, then of node 2p + 1.
   uint16_t* split;
+  // bf16 inputs: per node, an upper bound of the Euclidean norm of its f16 remainder times 2^-10,
+  // at (b * Hkv * pairs + pair) * 2 + (node & 1) (split_summaries_kernel writes it)
+  float* lonorm;
   int64_t pair_off[kMaxLevels];
   int64_t pairs;
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded
@@ -41,6 +44,7 @@ struct RouteArgs {
   int score;          // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
   bool bf16;
+  bool prefilter;     // bf16 LSE routing: score from the high parts first (route_prefilter_kernel)
   Levels lv;
 };
 

@@ -132,6 +132,29 @@ __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
     out = plane == 0 ? __builtin_bit_cast(uint4, hi) : __builtin_bit_cast(uint4, lo);
   }
   *reinterpret_cast<uint4*>(a.split + e * 8) = out;
+  // Remainder norm of each node of the block, |lo 2^-10|_2, rounded up: the kPieces threads of a
+  // block are one aligned group of lanes, so the sums are xor reductions within it.
+  float part = 0.f;
+  if (plane == 1) {
+    const f16x8 lo = __builtin_bit_cast(f16x8, out);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = (float)lo[j] * 0.0009765625f;   // 2^-10, exact
+      part = fmaf(v, v, part);
+    }
+  }
+  const int c = (q >> 2) & 1;
+  float p0 = c == 0 ? part : 0.f, p1 = c == 1 ? part : 0.f;
+#pragma unroll
+  for (int off = 1; off < kPieces; off <<= 1) {
+    p0 += __shfl_xor(p0, off, 64);
+    p1 += __shfl_xor(p1, off, 64);
+  }
+  // sums of D squares: relative rounding below 2^-17; sqrt within an ulp
+  if (q == 0) {
+    a.lonorm[blk * 2] = __builtin_sqrtf(p0) * 1.0000153f + 0x1p-60f;
+    a.lonorm[blk * 2 + 1] = __builtin_sqrtf(p1) * 1.0000153f + 0x1p-60f;
+  }
 }
 
 // ----------------------------------------------------------------------------- routing
@@ -257,9 +280,221 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   if (lane < width) a.cand[((int64_t)bh * a.n + t) * width + lane] = cand;
 }
 
+// ----------------------------------------------------------------------------- routing with a pre-filter
+// bf16 inputs, LSE score.  Each scored level first scores its candidates from the bf16 high parts
+// alone (half the bytes of the split rows, half the products) and bounds, per candidate, how far
+// route_kernel's score from the full split rows can lie from that estimate.  Only candidates whose
+// interval straddles the K-th place are scored again from the full split rows, with route_kernel's
+// arithmetic, so the kept set is route_kernel's:
+//  * a child logit from the split rows is fl(y_hi + fl(q_lo . lo) 2^-10), y_hi the high-part product
+//    (the same MFMA on the same operands, so the same value); |q_lo . lo| 2^-10 <= |q|_2 |lo 2^-10|_2
+//    (Cauchy-Schwarz; the float32 sum of the products adds at most 2^-17 of it), with the query norm
+//    rounded up here and the remainder norms in a.lonorm;
+//  * the pair LSE moves by at most its larger logit change (its gradient is a probability vector)
+//    and the head sum by the sum over heads; the rounding differences of the logit scaling, the
+//    exp2/log2 evaluation and the head sum are covered by 2^-20 (|score| + |z0| + |z1| + 1) per head;
+//  * with L = u - E and U = u + E around the estimate u: a candidate whose L exceeds the (K+1)-th
+//    largest U is in the split score's top K, one whose U is below the K-th largest L is not, and the
+//    rest are scored again and fill the remaining places by (score, then lower index).  Should the
+//    bounds ever leave a count that cannot be right, every candidate of the level is scored again.
+
+// The largest threshold that at least k lanes' keys reach (the k-th largest key), one ballot per bit.
+__device__ inline uint32_t kth_key(uint32_t key, int k) {
+  uint32_t thr = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = thr | (1u << bit);
+    if (__popcll(__ballot(key >= trial)) >= k) thr = trial;
+  }
+  return thr;
+}
+
+template <int D>
+struct HiTile {                                      // the high plane of 16 child rows
+  FragBF16<D> h;
+  float nrm;                                         // remainder bound of this lane's row (row col)
+  __device__ inline void load(const RouteArgs& a, const uint16_t* rows, const float* norms, int li, int child,
+                              int g) {
+    const uint16_t* r = rows + a.pair_off[li] * (4 * D) + (uint32_t)((child >> 1) * (4 * D) + 32 * (child & 1) + 8 * g);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) h.v[s] = *reinterpret_cast<const bf16x8*>(r + 64 * s);
+    nrm = norms[2 * a.pair_off[li] + child];
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_prefilter_kernel(RouteArgs a) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n) return;
+  const int bh = blockIdx.y;
+  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
+  const int g = lane >> 4, col = lane & 15;
+  const int width = 2 * a.top_k, K = a.top_k;
+  const float c2 = a.scale * 1.4426950408889634f;       // logits in base-2 units
+  const bool head_ok = col < a.group;
+
+  typedef RouteOps<__bf16, D> Ops;
+  typename Ops::Q qf;
+  float qsq = 0.f;                                     // this lane's part of |q_head|^2
+  if (head_ok) {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st +
+                         (int64_t)(kvh * a.group + col) * a.q_sh;
+    Ops::load_q(qf, qrow, g);
+    if (a.qpack) {                                     // the leaf stage's packed copy of this query group
+      bf16x8* dst = a.qpack + ((int64_t)bh * a.n + t) * (a.group * D / 8) + g * a.group + col;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) dst[4 * s * a.group] = qf.h.v[s];
+    }
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (float)qf.h.v[s][j];
+        qsq = fmaf(x, x, qsq);
+      }
+  } else {
+    Ops::zero_q(qf);
+  }
+  qsq += __shfl_xor(qsq, 16, 64);
+  qsq += __shfl_xor(qsq, 32, 64);
+  // |q_lo|_2 <= |q|_2 + sqrt(D) 2^-25 (f16 subnormals); sum and sqrt rounding below 2^-16
+  const float qn = __builtin_sqrtf(qsq) * 1.0000153f + 0x1p-21f;
+  const uint16_t* rows = a.split + (int64_t)bh * a.pairs * (4 * D);
+  const float* norms = a.lonorm + (int64_t)bh * a.pairs * 2;
+
+  int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
+  for (int level = a.lv.count; level >= 2; --level) {
+    const uint64_t valid = __ballot(cand >= 0);
+    const int n_valid = __popcll(valid);
+    const int child_size = a.lv.size[level - 2];
+    bool keep = cand >= 0;
+    auto child_ok = [&](int parent, int child) {
+      return parent >= 0 && child < child_size && node_first_key(level - 1, child) <= t;
+    };
+    if (n_valid > K) {
+      const int span = 64 - __clzll(valid);
+      const int tiles = (((2 * span + 15) / 16) + 1) & ~1;
+      auto child_of = [&](int nt, bool& ok) {
+        const int slot = 16 * nt + col;
+        const int parent = __shfl(cand, slot >> 1, 64);
+        const int child = 2 * parent + (slot & 1);
+        ok = child_ok(parent, child);
+        return ok ? child : 0;
+      };
+      float u = kNegInf, E = 0.f;                      // estimate and bound of candidate `lane`
+      auto do_tile = [&](int nt, HiTile<D>& cur, HiTile<D>& nxt, bool& ok_cur) {
+        const uint32_t rows_ok = (uint32_t)__ballot(ok_cur) >> (4 * g);
+        bool ok_n;
+        const int child_n = child_of(min(nt + 1, tiles - 1), ok_n);
+        nxt.load(a, rows, norms, level - 2, child_n, g);
+        ok_cur = ok_n;
+        const floatx4 acc = mma(cur.h, qf.h, floatx4{0.f, 0.f, 0.f, 0.f});
+        float nr[4];                                   // remainder bounds of rows 4g .. 4g + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nr[i] = __shfl(cur.nrm, 4 * g + i, 64);
+        float ps[2], pe[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float y0 = acc[2 * h], y1 = acc[2 * h + 1];
+          const bool ok1 = (rows_ok >> (2 * h + 1)) & 1u;
+          const float sc = pair_score(y0, y1, true, ok1, 0, a.scale, c2);
+          const float d0 = qn * nr[2 * h] * 1.001f + 0x1p-22f * fabsf(y0);
+          const float d1 = ok1 ? qn * nr[2 * h + 1] * 1.001f + 0x1p-22f * fabsf(y1) : 0.f;
+          const float z = (fabsf(y0) + (ok1 ? fabsf(y1) : 0.f)) * c2;
+          const float e = c2 * 1.0001f * fmaxf(d0, d1) + 0x1p-20f * (fabsf(sc) + z + 1.f);
+          ps[h] = row_sum_to_last(head_ok ? sc : 0.f);
+          pe[h] = row_sum_to_last(head_ok ? e : 0.f);
+        }
+        const int src = 16 * ((lane & 7) >> 1) + 15;
+        const float s0 = __shfl(ps[0], src, 64), s1 = __shfl(ps[1], src, 64);
+        const float e0 = __shfl(pe[0], src, 64), e1 = __shfl(pe[1], src, 64);
+        if ((lane >> 3) == nt) {
+          u = (lane & 1) ? s1 : s0;
+          E = (lane & 1) ? e1 : e0;
+        }
+      };
+      bool ok_t;
+      HiTile<D> ta, tb;
+      ta.load(a, rows, norms, level - 2, child_of(0, ok_t), g);
+      for (int nt = 0; nt < tiles; nt += 2) {
+        do_tile(nt, ta, tb, ok_t);
+        do_tile(nt + 1, tb, ta, ok_t);
+      }
+      // the interval [u - E', u + E'] holds route_kernel's score (E' also covers rounding here)
+      const bool vc = cand >= 0;
+      const float Ep = E * 1.0000003f + 0x1p-20f * fabsf(u) + 0x1p-40f;
+      const uint32_t kl = score_key(u - Ep, vc), ku = score_key(u + Ep, vc);
+      const uint32_t tl = kth_key(kl, K), tu = kth_key(ku, K + 1);
+      const bool in = vc && kl > tu;                   // in the top K whatever the full scores
+      const bool undecided = vc && !in && !(ku < tl);
+      const int n_in = __popcll(__ballot(in));
+      const uint64_t und = __ballot(undecided);
+      if (!(und == 0 && n_in == K)) {                  // wave-uniform
+        const bool redo_all = und == 0 || n_in > K;
+        const bool again = redo_all ? vc : undecided;
+        const uint64_t am = __ballot(again);
+        const int places = redo_all ? K : K - n_in;
+        keep = redo_all ? false : in;
+        if (places > 0) {
+          // the candidates to score again, compacted into lanes 0 .. n_again - 1
+          const int n_again = __popcll(am);
+          const int src_lane = nth_set_bit(am, lane < n_again ? lane : 0);
+          const int cs = __shfl(cand, src_lane, 64);
+          const int rc = lane < n_again ? cs : -1;
+          float ur = kNegInf;
+          const int rtiles = (2 * n_again + 15) / 16;
+          for (int nt = 0; nt < rtiles; ++nt) {
+            const int slot = 16 * nt + col;
+            const int parent = __shfl(rc, slot >> 1, 64);
+            const int child = 2 * parent + (slot & 1);
+            const bool ok = child_ok(parent, child);
+            typename Ops::Tile tile;
+            tile.load(a, rows, level - 2, ok ? child : 0, g);
+            const uint32_t rows_ok = (uint32_t)__ballot(ok) >> (4 * g);
+            const floatx4 acc = Ops::dot(tile, qf);
+            float pscore[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, 0,
+                                          a.scale, c2);
+              pscore[h] = row_sum_to_last(head_ok ? sc : 0.f);
+            }
+            const int src = 16 * ((lane & 7) >> 1) + 15;
+            const float s0 = __shfl(pscore[0], src, 64), s1 = __shfl(pscore[1], src, 64);
+            if ((lane >> 3) == nt) ur = (lane & 1) ? s1 : s0;
+          }
+          // back to the candidates' lanes: candidate lane i is entry mbcnt(am below i)
+          const int j = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(am >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)am, 0u));
+          const float ux = __shfl(ur, again ? j : 0, 64);
+          const bool best = keep_top_k(score_key(ux, again), places);   // the whole wave votes
+          keep = keep || (again && best);
+        }
+      } else {
+        keep = in;
+      }
+    }
+    // expand the survivors into their causally valid children
+    const uint64_t kept = __ballot(keep);
+    const int m = __popcll(kept);
+    const int p = lane >> 1;
+    const int src = nth_set_bit(kept, p < m ? p : 0);
+    const int parent = __shfl(cand, src, 64);
+    const int child = 2 * parent + (lane & 1);
+    cand = (p < m && child < child_size && node_first_key(level - 1, child) <= t) ? child : -1;
+  }
+  if (lane < width) a.cand[((int64_t)bh * a.n + t) * width + lane] = cand;
+}
+
 template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
+  if constexpr (sizeof(T) == 2) {
+    if (a.prefilter && a.score == 0) {
+      hipLaunchKernelGGL(route_prefilter_kernel<D>, grid, dim3(256), 0, s, a);
+      return launched(s);
+    }
+  }
   if (a.score == 1)
     hipLaunchKernelGGL((route_kernel<T, D, 1>), grid, dim3(256), 0, s, a);
   else if (a.score == 2)
