@@ -110,7 +110,7 @@ pisa_status hip_status(hipError_t e) {
 }
 
 struct SelectWorkspace {
-  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, lonorm, kpack, qpack, total;
+  size_t cand, leaf_u, pairs, leaf_off, items, n_items, split, split16, bounds, kpack, qpack, total;
   int n_windows, item_cap;
 };
 
@@ -139,8 +139,9 @@ SelectWorkspace select_layout(const pisa_cfg* c) {
   const size_t split_bytes = (size_t)split_blocks * c->head_dim * 8;
   const size_t kpack_bytes = bf16 ? (size_t)bh * m1 * pisa::kLeaf * c->head_dim * 2 : 0;
   const size_t qpack_bytes = bf16 ? (size_t)bh * c->seq_len * c->n_q_heads / c->n_kv_heads * c->head_dim * 2 : 0;
-  w.lonorm = align256(w.split + split_bytes);         // two floats per split block
-  w.kpack = align256(w.lonorm + (size_t)split_blocks * 8);
+  w.split16 = align256(w.split + split_bytes);        // the float16 copy: half the split bytes
+  w.bounds = align256(w.split16 + split_bytes / 2);   // (R, X) per node: four floats per block
+  w.kpack = align256(w.bounds + (size_t)split_blocks * 16);
   w.qpack = align256(w.kpack + kpack_bytes);
   w.total = align256(w.qpack + qpack_bytes);
   return w;
@@ -356,7 +357,8 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.n = N; r.top_k = cfg->top_k; r.scale = scale; r.bf16 = bf16; r.score = cfg->score;
   r.lv = make_levels(N, N);
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
-  r.lonorm = bf16 ? reinterpret_cast<float*>(base + w.lonorm) : nullptr;
+  r.split16 = bf16 ? reinterpret_cast<uint16_t*>(base + w.split16) : nullptr;
+  r.bounds = bf16 ? reinterpret_cast<float*>(base + w.bounds) : nullptr;
   r.prefilter = bf16 && cfg->score == PISA_SCORE_LSE && !pisa::route_exact();
   r.pairs = split_pairs(r.lv, r.pair_off);
   pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);

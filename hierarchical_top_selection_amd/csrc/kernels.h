@@ -28,9 +28,12 @@ struct RouteArgs {
   // (per b * Hkv: `pairs` blocks).  Line (plane, s), plane 0 = high / 1 = remainder, s < d / 32,
   // is 128 bytes: elements [32 s, 32 s + 32) of node 2p, then of node 2p + 1.
   uint16_t* split;
-  // bf16 inputs: per node, an upper bound of the Euclidean norm of its f16 remainder times 2^-10,
-  // at (b * Hkv * pairs + pair) * 2 + (node & 1) (split_summaries_kernel writes it)
-  float* lonorm;
+  // bf16 inputs, for the routing pre-filter: a float16 copy of the summaries, one plane of the
+  // same pair-block layout (2 d elements per block: line s holds elements [32 s, 32 s + 32) of node
+  // 2p, then of node 2p + 1), and per node two bounds (R, X) at ((b * Hkv * pairs + pair) * 2 +
+  // (node & 1)) * 2 (split_summaries_kernel writes both; route.hip states what they bound)
+  uint16_t* split16;
+  float* bounds;
   int64_t pair_off[kMaxLevels];
   int64_t pairs;
   int32_t* cand;      // [B*Hkv][N][2K] leaf candidates, -1 padded

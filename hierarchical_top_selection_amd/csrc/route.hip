@@ -101,6 +101,12 @@ template <int D> struct RouteOps<__bf16, D> {        // bf16 high part + f16 rem
 // block, q = 8 line + 4 c + g with elements [32 s + 8 g, +8) of node 2p + c (zero past the
 // level's end).  hi = bf16(x) to nearest; the remainder x - hi is exact in fp32, is scaled by
 // 2^10 and rounded to the nearest f16 after clamping to its range.
+// For the routing pre-filter it also writes the float16 copy x16 = f16(x) (clamped to the f16
+// range; plane-0 threads write the piece of their eight elements) and, per node, the bounds R and
+// X of route_prefilter_kernel from five sums of squares over the node's d elements: plane-0
+// threads add xi = x - x16, hi and x16, plane-1 threads rho = (x - hi) - lo 2^-10 (the remainder's
+// own rounding) and lo 2^-10.  The kPieces threads of a block are one aligned group of lanes, so
+// the per-node sums are xor reductions within it.
 template <int D>
 __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
   constexpr int kPieces = D / 2;                      // 16-byte pieces per pair block
@@ -112,48 +118,66 @@ __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
   const int64_t pr = blk % a.pairs;
   int li = 0;
   while (li + 1 < a.lv.count && pr >= a.pair_off[li + 1]) ++li;
-  const int64_t node = 2 * (pr - a.pair_off[li]) + ((q >> 2) & 1);
+  const int c = (q >> 2) & 1;
+  const int64_t node = 2 * (pr - a.pair_off[li]) + c;
   const int line = q >> 3, g = q & 3;
   const int plane = line / (D / 32), s = line % (D / 32);
-  uint4 out = make_uint4(0u, 0u, 0u, 0u);
+  uint4 out = make_uint4(0u, 0u, 0u, 0u), out16 = make_uint4(0u, 0u, 0u, 0u);
+  float sq[5] = {0.f, 0.f, 0.f, 0.f, 0.f};            // xi, hi, x16 (plane 0) | rho, lo (plane 1)
   if (node < a.lv.size[li]) {
     const float* src = a.pyr + ((int64_t)bh * a.lv.nodes + a.lv.offset[li] + node) * D + 32 * s + 8 * g;
     const float4 x0 = *reinterpret_cast<const float4*>(src);
     const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
     const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     bf16x8 hi;
-    f16x8 lo;
+    f16x8 lo, x16;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       hi[j] = (__bf16)x[j];
       const float r = (x[j] - (float)hi[j]) * 1024.f;
       lo[j] = (_Float16)fminf(fmaxf(r, -65504.f), 65504.f);
+      x16[j] = (_Float16)fminf(fmaxf(x[j], -65504.f), 65504.f);
+      if (plane == 0) {
+        const float xi = x[j] - (float)x16[j], h = (float)hi[j], y = (float)x16[j];
+        sq[0] = fmaf(xi, xi, sq[0]);
+        sq[1] = fmaf(h, h, sq[1]);
+        sq[2] = fmaf(y, y, sq[2]);
+      } else {
+        const float l = (float)lo[j] * 0.0009765625f;  // 2^-10, exact
+        const float rho = (x[j] - (float)hi[j]) - l;
+        sq[3] = fmaf(rho, rho, sq[3]);
+        sq[4] = fmaf(l, l, sq[4]);
+      }
     }
     out = plane == 0 ? __builtin_bit_cast(uint4, hi) : __builtin_bit_cast(uint4, lo);
+    out16 = __builtin_bit_cast(uint4, x16);
   }
   *reinterpret_cast<uint4*>(a.split + e * 8) = out;
-  // Remainder norm of each node of the block, |lo 2^-10|_2, rounded up: the kPieces threads of a
-  // block are one aligned group of lanes, so the sums are xor reductions within it.
-  float part = 0.f;
-  if (plane == 1) {
-    const f16x8 lo = __builtin_bit_cast(f16x8, out);
+  if (plane == 0) *reinterpret_cast<uint4*>(a.split16 + (blk * (kPieces / 2) + q) * 8) = out16;
+  float n0[5], n1[5];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = (float)lo[j] * 0.0009765625f;   // 2^-10, exact
-      part = fmaf(v, v, part);
+  for (int i = 0; i < 5; ++i) {
+    n0[i] = c == 0 ? sq[i] : 0.f;
+    n1[i] = c == 1 ? sq[i] : 0.f;
+  }
+#pragma unroll
+  for (int off = 1; off < kPieces; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      n0[i] += __shfl_xor(n0[i], off, 64);
+      n1[i] += __shfl_xor(n1[i], off, 64);
     }
-  }
-  const int c = (q >> 2) & 1;
-  float p0 = c == 0 ? part : 0.f, p1 = c == 1 ? part : 0.f;
-#pragma unroll
-  for (int off = 1; off < kPieces; off <<= 1) {
-    p0 += __shfl_xor(p0, off, 64);
-    p1 += __shfl_xor(p1, off, 64);
-  }
-  // sums of D squares: relative rounding below 2^-17; sqrt within an ulp
   if (q == 0) {
-    a.lonorm[blk * 2] = __builtin_sqrtf(p0) * 1.0000153f + 0x1p-60f;
-    a.lonorm[blk * 2 + 1] = __builtin_sqrtf(p1) * 1.0000153f + 0x1p-60f;
+    // a sum of d squares rounds by less than 2^-17 relative and sqrt by an ulp: 2^-15 covers both
+    float* bnd = a.bounds + blk * 4;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float* n = k == 0 ? n0 : n1;
+      const float xi = __builtin_sqrtf(n[0]), hn = __builtin_sqrtf(n[1]), x16n = __builtin_sqrtf(n[2]);
+      const float rho = __builtin_sqrtf(n[3]), lon = __builtin_sqrtf(n[4]);
+      bnd[2 * k] = (rho + xi) * 1.0000306f + 0x1p-15f * 1.01f * (hn + lon + x16n) + 0x1p-60f;   // R
+      bnd[2 * k + 1] = (lon + x16n) * 1.0000306f + 0x1p-60f;                                  // X
+    }
   }
 }
 
@@ -281,15 +305,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 }
 
 // ----------------------------------------------------------------------------- routing with a pre-filter
-// bf16 inputs, LSE score.  Each scored level first scores its candidates from the bf16 high parts
-// alone (half the bytes of the split rows, half the products) and bounds, per candidate, how far
-// route_kernel's score from the full split rows can lie from that estimate.  Only candidates whose
-// interval straddles the K-th place are scored again from the full split rows, with route_kernel's
+// bf16 inputs, LSE score.  Each scored level first scores its candidates from a float16 copy of the
+// summaries (half the bytes of the split rows, half the products) and bounds, per candidate, how
+// far route_kernel's score from the split rows can lie from that estimate.  Only candidates whose
+// interval straddles the K-th place are scored again from the split rows, with route_kernel's
 // arithmetic, so the kept set is route_kernel's:
-//  * a child logit from the split rows is fl(y_hi + fl(q_lo . lo) 2^-10), y_hi the high-part product
-//    (the same MFMA on the same operands, so the same value); |q_lo . lo| 2^-10 <= |q|_2 |lo 2^-10|_2
-//    (Cauchy-Schwarz; the float32 sum of the products adds at most 2^-17 of it), with the query norm
-//    rounded up here and the remainder norms in a.lonorm;
+//  * per child and head, with q the bf16 query, q_lo its f16 copy (eps = q - q_lo), x the node,
+//    hi, lo its split parts, rho = (x - hi) - lo 2^-10, x16 = f16(x), xi = x - x16, and g the
+//    relative error of a float32 sum of d products (under 2^-16 for d <= 128, rounding or not):
+//      |y_split - q.x| <= |q| (|rho| + g (|hi| + |lo 2^-10|)) + |eps| |lo 2^-10| + 2^-24 |y_split|,
+//      |y_16 - q.x| <= |q| (|xi| + g |x16|) + |eps| |x16|   (Cauchy-Schwarz, Euclidean norms),
+//    so |y_split - y_16| <= |q| R + |eps| X (1 + g) + 2^-24 |y_split| with the per-node bounds
+//    R = |rho| + |xi| + g (|hi| + |lo 2^-10| + |x16|) and X = |lo 2^-10| + |x16| of
+//    split_summaries_kernel (rounded up), and the query norms rounded up here;
 //  * the pair LSE moves by at most its larger logit change (its gradient is a probability vector)
 //    and the head sum by the sum over heads; the rounding differences of the logit scaling, the
 //    exp2/log2 evaluation and the head sum are covered by 2^-20 (|score| + |z0| + |z1| + 1) per head;
@@ -310,15 +338,15 @@ __device__ inline uint32_t kth_key(uint32_t key, int k) {
 }
 
 template <int D>
-struct HiTile {                                      // the high plane of 16 child rows
-  FragBF16<D> h;
-  float nrm;                                         // remainder bound of this lane's row (row col)
-  __device__ inline void load(const RouteArgs& a, const uint16_t* rows, const float* norms, int li, int child,
+struct F16Tile {                                     // the float16 copy of 16 child rows
+  FragF16<D> f;
+  float2 rx;                                         // (R, X) of this lane's row (row col)
+  __device__ inline void load(const RouteArgs& a, const uint16_t* rows16, const float2* bounds, int li, int child,
                               int g) {
-    const uint16_t* r = rows + a.pair_off[li] * (4 * D) + (uint32_t)((child >> 1) * (4 * D) + 32 * (child & 1) + 8 * g);
+    const uint16_t* r = rows16 + a.pair_off[li] * (2 * D) + (uint32_t)((child >> 1) * (2 * D) + 32 * (child & 1) + 8 * g);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) h.v[s] = *reinterpret_cast<const bf16x8*>(r + 64 * s);
-    nrm = norms[2 * a.pair_off[li] + child];
+    for (int s = 0; s < D / 32; ++s) f.v[s] = *reinterpret_cast<const f16x8*>(r + 64 * s);
+    rx = bounds[2 * a.pair_off[li] + child];
   }
 };
 
@@ -336,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 
   typedef RouteOps<__bf16, D> Ops;
   typename Ops::Q qf;
-  float qsq = 0.f;                                     // this lane's part of |q_head|^2
+  float qsq = 0.f, qdsq = 0.f;                         // this lane's parts of |q|^2 and |q - q_lo|^2
   if (head_ok) {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)t * a.q_st +
                          (int64_t)(kvh * a.group + col) * a.q_sh;
@@ -350,18 +378,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = (float)qf.h.v[s][j];
+        const float x = (float)qf.h.v[s][j], dx = x - (float)qf.l.v[s][j];
         qsq = fmaf(x, x, qsq);
+        qdsq = fmaf(dx, dx, qdsq);
       }
   } else {
     Ops::zero_q(qf);
   }
   qsq += __shfl_xor(qsq, 16, 64);
   qsq += __shfl_xor(qsq, 32, 64);
-  // |q_lo|_2 <= |q|_2 + sqrt(D) 2^-25 (f16 subnormals); sum and sqrt rounding below 2^-16
-  const float qn = __builtin_sqrtf(qsq) * 1.0000153f + 0x1p-21f;
+  qdsq += __shfl_xor(qdsq, 16, 64);
+  qdsq += __shfl_xor(qdsq, 32, 64);
+  // |q|_2 and |q - q_lo|_2 of this lane's head, rounded up (sum and sqrt rounding below 2^-16)
+  const float qn = __builtin_sqrtf(qsq) * 1.0000153f + 0x1p-60f;
+  const float qd = __builtin_sqrtf(qdsq) * 1.0000153f + 0x1p-60f;
   const uint16_t* rows = a.split + (int64_t)bh * a.pairs * (4 * D);
-  const float* norms = a.lonorm + (int64_t)bh * a.pairs * 2;
+  const uint16_t* rows16 = a.split16 + (int64_t)bh * a.pairs * (2 * D);
+  const float2* bounds = reinterpret_cast<const float2*>(a.bounds) + (int64_t)bh * a.pairs * 2;
 
   int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
   for (int level = a.lv.count; level >= 2; --level) {
@@ -383,24 +416,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         return ok ? child : 0;
       };
       float u = kNegInf, E = 0.f;                      // estimate and bound of candidate `lane`
-      auto do_tile = [&](int nt, HiTile<D>& cur, HiTile<D>& nxt, bool& ok_cur) {
+      auto do_tile = [&](int nt, F16Tile<D>& cur, F16Tile<D>& nxt, bool& ok_cur) {
         const uint32_t rows_ok = (uint32_t)__ballot(ok_cur) >> (4 * g);
         bool ok_n;
         const int child_n = child_of(min(nt + 1, tiles - 1), ok_n);
-        nxt.load(a, rows, norms, level - 2, child_n, g);
+        nxt.load(a, rows16, bounds, level - 2, child_n, g);
         ok_cur = ok_n;
-        const floatx4 acc = mma(cur.h, qf.h, floatx4{0.f, 0.f, 0.f, 0.f});
-        float nr[4];                                   // remainder bounds of rows 4g .. 4g + 3
+        const floatx4 acc = mma(cur.f, qf.l, floatx4{0.f, 0.f, 0.f, 0.f});
+        float br[4], bx[4];                            // R and X of rows 4g .. 4g + 3
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nr[i] = __shfl(cur.nrm, 4 * g + i, 64);
+        for (int i = 0; i < 4; ++i) {
+          br[i] = __shfl(cur.rx.x, 4 * g + i, 64);
+          bx[i] = __shfl(cur.rx.y, 4 * g + i, 64);
+        }
+        // |y_split - y_16| <= (|q| R + |eps| X (1 + 2^-15) + 2^-24 |y_16|) (1 + 2^-23), plus 2^-40
+        // for denormal flushes
+        auto dev = [&](int i, float y) {
+          return (qn * br[i] + qd * bx[i] * 1.0001f + 0x1p-24f * fabsf(y)) * 1.0001f + 0x1p-40f;
+        };
         float ps[2], pe[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const float y0 = acc[2 * h], y1 = acc[2 * h + 1];
           const bool ok1 = (rows_ok >> (2 * h + 1)) & 1u;
           const float sc = pair_score(y0, y1, true, ok1, 0, a.scale, c2);
-          const float d0 = qn * nr[2 * h] * 1.001f + 0x1p-22f * fabsf(y0);
-          const float d1 = ok1 ? qn * nr[2 * h + 1] * 1.001f + 0x1p-22f * fabsf(y1) : 0.f;
+          const float d0 = dev(2 * h, y0);
+          const float d1 = ok1 ? dev(2 * h + 1, y1) : 0.f;
           const float z = (fabsf(y0) + (ok1 ? fabsf(y1) : 0.f)) * c2;
           const float e = c2 * 1.0001f * fmaxf(d0, d1) + 0x1p-20f * (fabsf(sc) + z + 1.f);
           ps[h] = row_sum_to_last(head_ok ? sc : 0.f);
@@ -415,8 +456,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         }
       };
       bool ok_t;
-      HiTile<D> ta, tb;
-      ta.load(a, rows, norms, level - 2, child_of(0, ok_t), g);
+      F16Tile<D> ta, tb;
+      ta.load(a, rows16, bounds, level - 2, child_of(0, ok_t), g);
       for (int nt = 0; nt < tiles; nt += 2) {
         do_tile(nt, ta, tb, ok_t);
         do_tile(nt + 1, tb, ta, ok_t);

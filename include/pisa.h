@@ -167,20 +167,20 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  * inputs the float32 summaries above the leaves enter the dot products as a
  * bf16 part plus a float16 remainder scaled by 2^10 (about 2^-20 relative
  * error per element); float32 inputs use the summaries as they are.  With
- * the LSE score, bf16 routing first scores each level from the bf16 parts
- * alone with a bound on the remainder's contribution, and scores again from
- * both parts only the candidates the bound leaves undecided; the kept sets are
- * those of scoring every candidate from both parts (which the environment
- * variable PISA_ROUTE_EXACT=1 forces).
+ * the LSE score, bf16 routing first scores each level from a float16 copy of
+ * the summaries with a bound on its distance to the split score, and scores
+ * again from both split parts only the candidates the bound leaves
+ * undecided; the kept sets are those of scoring every candidate from both
+ * parts (which the environment variable PISA_ROUTE_EXACT=1 forces).
  *   q, k    : [B][N][H_q][d] and [B][N][H_kv][d], cfg->dtype
  *   pyr     : pyramid of k built with n = N (capacity N)
  *   sel     : int32 [B][H_kv][N][K] output, ascending, -1 padded
  *   sel_u   : optional float32 [B][H_kv][N][K] output (NULL to skip): the leaf
  *             score u of each selected block, -inf on padding
  *   ws      : workspace of >= pisa_select_workspace_bytes(cfg) bytes (for
- *             bf16 inputs it also holds the split summaries with a remainder
- *             norm per node, and packed copies of K and Q, about the size of
- *             q plus k); its first
+ *             bf16 inputs it also holds the split summaries, their float16
+ *             copy with two bounds per node, and packed copies of K and Q,
+ *             about the size of q plus k); its first
  *             B*H_kv*N*2K int32 hold the leaf candidates of each token (-1
  *             padded) after the call
  */
