@@ -141,6 +141,7 @@ def compulsory_bytes(w: W.Workload) -> dict:
         "pyramid_top_kernel": bh * (sizes[3] if len(sizes) > 3 else 0) * d * 4 + bh * sum(sizes[4:]) * d * 4,
         "split_summaries_kernel": bh * nodes * d * 4 + bh * sum(-(-m // 2) for m in sizes) * 8 * d,
         "route_kernel": q_bytes + (bh * N * G * d * 2 if w.dtype == "bf16" else 0) + slots,
+        "route_prefilter_kernel": q_bytes + bh * N * G * d * 2 + slots,
         "cluster_kernel": 2 * slots + bh * windows * (m1 + 1) * 4,
         "pack_blocks_kernel": bh * N * d * 2 + packed,
         "leaf_lse_kernel": bh * N * G * d * 2 + packed + 2 * slots,
@@ -183,7 +184,7 @@ def stage_kernels(w: W.Workload) -> dict:
     levels = len(level_sizes(w.seq_len))
     return {
         "pyramid": ["pyramid_leaves_kernel"] + (["pyramid_top_kernel"] if levels > 4 else []),
-        "select": (["split_summaries_kernel"] if bf16 else []) + ["route_kernel", "cluster_kernel"]
+        "select": (["split_summaries_kernel", "route_prefilter_kernel"] if bf16 else ["route_kernel"]) + ["cluster_kernel"]
                   + (["pack_blocks_kernel"] if bf16 else []) + ["leaf_lse_kernel", "topk_kernel"],
         "attention": (["pack_blocks_kernel"] + (ORDER_KERNELS if level_sizes(w.seq_len)[0] <= 16384 else [])
                       + ["attention_bf16_kernel", "attention_bf16_kernel"] if bf16 else ["attention_f32_kernel"]),
@@ -511,6 +512,7 @@ KERNEL_SOURCES = {
     "pyramid_top_kernel": ("pyramid.hip", "pyramid_dev.h") + _COMMON,
     "split_summaries_kernel": ("route.hip",) + _COMMON,
     "route_kernel": ("route.hip",) + _COMMON,
+    "route_prefilter_kernel": ("route.hip",) + _COMMON,
     "cluster_kernel": ("cluster.hip",) + _COMMON,
     "pack_blocks_kernel": ("pack.hip",) + _COMMON,
     "leaf_lse_kernel": ("leaf_lse.hip",) + _COMMON,

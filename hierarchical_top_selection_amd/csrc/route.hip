@@ -319,8 +319,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 //    R = |rho| + |xi| + g (|hi| + |lo 2^-10| + |x16|) and X = |lo 2^-10| + |x16| of
 //    split_summaries_kernel (rounded up), and the query norms rounded up here;
 //  * the pair LSE moves by at most its larger logit change (its gradient is a probability vector)
-//    and the head sum by the sum over heads; the rounding differences of the logit scaling, the
-//    exp2/log2 evaluation and the head sum are covered by 2^-20 (|score| + |z0| + |z1| + 1) per head;
+//    and the head sum by the sum over heads.  R and X are the same for every head, so the sum over
+//    heads only needs QN = sum |q_h| and QD = sum |eps_h| of the token, and a candidate lane bounds
+//    its score from the (R, X) of its two children alone.  The rounding differences of the logit
+//    scaling, the exp2/log2 evaluation and the head sum are at most 2^-20 (|z0| + |z1| + 1) per
+//    head, with |z_i| <= c2 (|q_h| + |eps_h|) X_i (1 + g);
 //  * with L = u - E and U = u + E around the estimate u: a candidate whose L exceeds the (K+1)-th
 //    largest U is in the split score's top K, one whose U is below the K-th largest L is not, and the
 //    rest are scored again and fill the remaining places by (score, then lower index).  Should the
@@ -340,13 +343,10 @@ __device__ inline uint32_t kth_key(uint32_t key, int k) {
 template <int D>
 struct F16Tile {                                     // the float16 copy of 16 child rows
   FragF16<D> f;
-  float2 rx;                                         // (R, X) of this lane's row (row col)
-  __device__ inline void load(const RouteArgs& a, const uint16_t* rows16, const float2* bounds, int li, int child,
-                              int g) {
+  __device__ inline void load(const RouteArgs& a, const uint16_t* rows16, int li, int child, int g) {
     const uint16_t* r = rows16 + a.pair_off[li] * (2 * D) + (uint32_t)((child >> 1) * (2 * D) + 32 * (child & 1) + 8 * g);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) f.v[s] = *reinterpret_cast<const f16x8*>(r + 64 * s);
-    rx = bounds[2 * a.pair_off[li] + child];
   }
 };
 
@@ -392,9 +392,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   // |q|_2 and |q - q_lo|_2 of this lane's head, rounded up (sum and sqrt rounding below 2^-16)
   const float qn = __builtin_sqrtf(qsq) * 1.0000153f + 0x1p-60f;
   const float qd = __builtin_sqrtf(qdsq) * 1.0000153f + 0x1p-60f;
+  // QN = sum over the group's heads of |q_h|, QD of |eps_h| (sums of positive terms, rounded up)
+  const float qn_sum = row_sum_to_last(head_ok ? qn : 0.f), qd_sum = row_sum_to_last(head_ok ? qd : 0.f);
+  const float QN = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qn_sum), 15)) * 1.000001f;
+  const float QD = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qd_sum), 15)) * 1.000001f;
   const uint16_t* rows = a.split + (int64_t)bh * a.pairs * (4 * D);
   const uint16_t* rows16 = a.split16 + (int64_t)bh * a.pairs * (2 * D);
-  const float2* bounds = reinterpret_cast<const float2*>(a.bounds) + (int64_t)bh * a.pairs * 2;
+  const float4* bounds = reinterpret_cast<const float4*>(a.bounds) + (int64_t)bh * a.pairs;
 
   int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
   for (int level = a.lv.count; level >= 2; --level) {
@@ -415,53 +419,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         ok = child_ok(parent, child);
         return ok ? child : 0;
       };
-      float u = kNegInf, E = 0.f;                      // estimate and bound of candidate `lane`
+      // (R0, X0, R1, X1) of this lane's candidate's two children, for its bound after the tiles
+      const float4 b4 = bounds[a.pair_off[level - 2] + (cand >= 0 ? cand : 0)];
+      float u = kNegInf;                               // estimate of candidate `lane`
       auto do_tile = [&](int nt, F16Tile<D>& cur, F16Tile<D>& nxt, bool& ok_cur) {
         const uint32_t rows_ok = (uint32_t)__ballot(ok_cur) >> (4 * g);
         bool ok_n;
         const int child_n = child_of(min(nt + 1, tiles - 1), ok_n);
-        nxt.load(a, rows16, bounds, level - 2, child_n, g);
+        nxt.load(a, rows16, level - 2, child_n, g);
         ok_cur = ok_n;
         const floatx4 acc = mma(cur.f, qf.l, floatx4{0.f, 0.f, 0.f, 0.f});
-        float br[4], bx[4];                            // R and X of rows 4g .. 4g + 3
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          br[i] = __shfl(cur.rx.x, 4 * g + i, 64);
-          bx[i] = __shfl(cur.rx.y, 4 * g + i, 64);
-        }
-        // |y_split - y_16| <= (|q| R + |eps| X (1 + 2^-15) + 2^-24 |y_16|) (1 + 2^-23), plus 2^-40
-        // for denormal flushes
-        auto dev = [&](int i, float y) {
-          return (qn * br[i] + qd * bx[i] * 1.0001f + 0x1p-24f * fabsf(y)) * 1.0001f + 0x1p-40f;
-        };
-        float ps[2], pe[2];
+        float ps[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float y0 = acc[2 * h], y1 = acc[2 * h + 1];
-          const bool ok1 = (rows_ok >> (2 * h + 1)) & 1u;
-          const float sc = pair_score(y0, y1, true, ok1, 0, a.scale, c2);
-          const float d0 = dev(2 * h, y0);
-          const float d1 = ok1 ? dev(2 * h + 1, y1) : 0.f;
-          const float z = (fabsf(y0) + (ok1 ? fabsf(y1) : 0.f)) * c2;
-          const float e = c2 * 1.0001f * fmaxf(d0, d1) + 0x1p-20f * (fabsf(sc) + z + 1.f);
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, 0, a.scale, c2);
           ps[h] = row_sum_to_last(head_ok ? sc : 0.f);
-          pe[h] = row_sum_to_last(head_ok ? e : 0.f);
         }
         const int src = 16 * ((lane & 7) >> 1) + 15;
         const float s0 = __shfl(ps[0], src, 64), s1 = __shfl(ps[1], src, 64);
-        const float e0 = __shfl(pe[0], src, 64), e1 = __shfl(pe[1], src, 64);
-        if ((lane >> 3) == nt) {
-          u = (lane & 1) ? s1 : s0;
-          E = (lane & 1) ? e1 : e0;
-        }
+        if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
       };
       bool ok_t;
       F16Tile<D> ta, tb;
-      ta.load(a, rows16, bounds, level - 2, child_of(0, ok_t), g);
+      ta.load(a, rows16, level - 2, child_of(0, ok_t), g);
       for (int nt = 0; nt < tiles; nt += 2) {
         do_tile(nt, ta, tb, ok_t);
         do_tile(nt + 1, tb, ta, ok_t);
       }
+      // E: the sum over heads of c2 max_i (|q_h| R_i + |eps_h| X_i (1 + 2^-15) + 2^-24 |y_i|) (1 + 2^-23),
+      // with |y_i| <= (|q_h| + |eps_h|) X_i (1 + g), plus the rounding slack 2^-20 (|z0| + |z1| + 1)
+      // per head, here doubled
+      const float rmax = fmaxf(b4.x, b4.z), xmax = fmaxf(b4.y, b4.w);
+      const float E = c2 * 1.001f * (rmax * QN + xmax * (QD * 1.0001f + 0x1p-23f * (QN + QD))) +
+                      0x1p-19f * (c2 * (QN + QD) * (b4.y + b4.w) * 1.001f + (float)a.group) + 0x1p-40f;
       // the interval [u - E', u + E'] holds route_kernel's score (E' also covers rounding here)
       const bool vc = cand >= 0;
       const float Ep = E * 1.0000003f + 0x1p-20f * fabsf(u) + 0x1p-40f;
