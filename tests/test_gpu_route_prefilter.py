@@ -22,20 +22,28 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# (B, N, Hq, Hkv, d, K, planted blocks per 1024 leaves, key shift, seed)
+# (B, N, Hq, Hkv, d, K, planted blocks per 1024 leaves, key shift, seed, regime)
+# Regimes beyond N(0,1): "ties" (every key the same, so every score ties and the lower index
+# decides), "huge" (keys of order 1e6: summaries beyond the float16 range, clamped, so the bounds
+# must send those candidates to the split rows), "tiny" (keys of order 1e-6: float16 subnormal
+# summaries) and "subq" (queries with elements below the float16 normal range, so q - q_lo != 0).
 CASES = [
-    (1, 262144, 16, 1, 128, 16, 5, 2.0, 1),
-    (2, 32768, 32, 2, 128, 32, 8, 2.0, 2),
-    (1, 65536, 16, 1, 128, 8, 16, 3.0, 3),
-    (2, 20000, 16, 2, 64, 12, 8, 2.0, 4),
-    (1, 9000, 8, 8, 128, 5, 4, 1.0, 5),
-    (3, 3000, 4, 2, 128, 3, 0, 0.0, 6),
-    (1, 5000, 16, 16, 64, 1, 32, 4.0, 7),
+    (1, 262144, 16, 1, 128, 16, 5, 2.0, 1, "normal"),
+    (2, 32768, 32, 2, 128, 32, 8, 2.0, 2, "normal"),
+    (1, 65536, 16, 1, 128, 8, 16, 3.0, 3, "normal"),
+    (2, 20000, 16, 2, 64, 12, 8, 2.0, 4, "normal"),
+    (1, 9000, 8, 8, 128, 5, 4, 1.0, 5, "normal"),
+    (3, 3000, 4, 2, 128, 3, 0, 0.0, 6, "normal"),
+    (1, 5000, 16, 16, 64, 1, 32, 4.0, 7, "normal"),
+    (1, 6000, 16, 1, 128, 8, 0, 0.0, 8, "ties"),
+    (1, 6000, 16, 1, 128, 8, 8, 2.0, 9, "huge"),
+    (1, 6000, 16, 1, 128, 8, 8, 2.0, 10, "tiny"),
+    (1, 6000, 8, 1, 64, 4, 8, 2.0, 11, "subq"),
 ]
 
 
 def draw(case):
-    B, N, Hq, Hkv, d, K, plant, shift, seed = case
+    B, N, Hq, Hkv, d, K, plant, shift, seed, regime = case
     gen = torch.Generator(device=H.DEV)
     gen.manual_seed(seed)
     u = torch.randn(d, generator=gen, device=H.DEV)
@@ -48,6 +56,14 @@ def draw(case):
         for h in range(Hkv):
             for j in torch.randperm(m1, generator=gen, device=H.DEV)[:n_plant].tolist():
                 k[b, 64 * j:64 * j + 64, h] += shift * u
+    if regime == "ties":
+        k = torch.full_like(k, 0.375)
+    elif regime == "huge":
+        k = k * 1e6
+    elif regime == "tiny":
+        k = k * 1e-6
+    elif regime == "subq":
+        q = torch.where(torch.rand(q.shape, generator=gen, device=H.DEV) < 0.05, q * 1e-6, q)
     return q.to(torch.bfloat16), k.to(torch.bfloat16)
 
 
@@ -86,5 +102,5 @@ def test_prefilter_keeps_what_exact_routing_keeps(tmp_path):
     for i, case in enumerate(CASES):
         for name in (f"cand{i}", f"sel{i}"):
             diff = int((here[name] != there[name]).sum())
-            H.log(f"[route pre-filter] case {case[:6]} {name[:-len(str(i))]}: {diff} differing entries")
+            H.log(f"[route pre-filter] case {case[:6]} {case[9]} {name[:-len(str(i))]}: {diff} differing entries")
             assert diff == 0, (case, name)
