@@ -311,8 +311,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 // interval straddles the K-th place are scored again from the split rows, with route_kernel's
 // arithmetic, so the kept set is route_kernel's:
 //  * per child and head, with q the bf16 query, q_lo its f16 copy (eps = q - q_lo), x the node,
-//    hi, lo its split parts, rho = (x - hi) - lo 2^-10, x16 = f16(x), xi = x - x16, and g the
-//    relative error of a float32 sum of d products (under 2^-16 for d <= 128, rounding or not):
+//    hi, lo its split parts, rho = (x - hi) - lo 2^-10, x16 = f16(x), xi = x - x16, and g = 2^-15
+//    a bound on the relative error of a float32 sum of d <= 128 products (132 additions at most,
+//    each off by 2^-23 even when truncating):
 //      |y_split - q.x| <= |q| (|rho| + g (|hi| + |lo 2^-10|)) + |eps| |lo 2^-10| + 2^-24 |y_split|,
 //      |y_16 - q.x| <= |q| (|xi| + g |x16|) + |eps| |x16|   (Cauchy-Schwarz, Euclidean norms),
 //    so |y_split - y_16| <= |q| R + |eps| X (1 + g) + 2^-24 |y_split| with the per-node bounds
