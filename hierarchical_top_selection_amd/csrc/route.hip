@@ -181,6 +181,19 @@ __global__ __launch_bounds__(256) void split_summaries_kernel(RouteArgs a) {
   }
 }
 
+// The levels from the root down keep every causally valid node while there are at most K of them.
+// Returns the first level with more than K valid nodes (1 if none: the valid leaves are then the
+// candidates) and that level's valid count: its candidates are nodes 0 .. count - 1, in the order
+// the expansions above it would list them.
+__device__ inline int first_scored_level(const RouteArgs& a, int t, int& n_valid) {
+  int level = a.lv.count;
+  for (;;) {
+    n_valid = (int)min((int64_t)a.lv.size[level - 1], ((int64_t)t >> (level - 1)) / kLeaf + 1);
+    if (level == 1 || n_valid > a.top_k) return level;
+    --level;
+  }
+}
+
 // ----------------------------------------------------------------------------- routing
 // kScore: the candidate score (pisa_score), fixed per instantiation so only its code is live.
 template <typename T, int D, int kScore>
@@ -212,8 +225,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   }
   const typename Ops::Row* rows = Ops::rows(a, bh);
 
-  int cand = lane == 0 ? 0 : -1;                       // A^(L) = {root}
-  for (int level = a.lv.count; level >= 2; --level) {
+  int n_first;
+  const int first = first_scored_level(a, t, n_first);
+  int cand = lane < n_first ? lane : -1;              // every valid node of the first scored level
+  for (int level = first; level >= 2; --level) {
     const uint64_t valid = __ballot(cand >= 0);
     const int n_valid = __popcll(valid);
     const int child_size = a.lv.size[level - 2];
@@ -339,19 +354,6 @@ __device__ inline uint32_t kth_key(uint32_t key, int k) {
     if (__popcll(__ballot(key >= trial)) >= k) thr = trial;
   }
   return thr;
-}
-
-// The levels from the root down keep every causally valid node while there are at most K of them.
-// Returns the first level with more than K valid nodes (1 if none: the valid leaves are then the
-// candidates) and that level's valid count: its candidates are nodes 0 .. count - 1, in the order
-// the expansions above it would list them.
-__device__ inline int first_scored_level(const RouteArgs& a, int t, int& n_valid) {
-  int level = a.lv.count;
-  for (;;) {
-    n_valid = (int)min((int64_t)a.lv.size[level - 1], ((int64_t)t >> (level - 1)) / kLeaf + 1);
-    if (level == 1 || n_valid > a.top_k) return level;
-    --level;
-  }
 }
 
 template <int D>
