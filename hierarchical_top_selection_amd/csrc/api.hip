@@ -359,7 +359,7 @@ pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k
   r.split = bf16 ? reinterpret_cast<uint16_t*>(base + w.split) : nullptr;
   r.split16 = bf16 ? reinterpret_cast<uint16_t*>(base + w.split16) : nullptr;
   r.bounds = bf16 ? reinterpret_cast<float*>(base + w.bounds) : nullptr;
-  r.prefilter = bf16 && cfg->score == PISA_SCORE_LSE && !pisa::route_exact();
+  r.prefilter = bf16 && !pisa::route_exact();
   r.pairs = split_pairs(r.lv, r.pair_off);
   pisa::bf16x8* kpack = reinterpret_cast<pisa::bf16x8*>(base + w.kpack);
   pisa::bf16x8* qpack = reinterpret_cast<pisa::bf16x8*>(base + w.qpack);

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 }
 
 // ----------------------------------------------------------------------------- routing with a pre-filter
-// bf16 inputs, LSE score.  Each scored level first scores its candidates from a float16 copy of the
+// bf16 inputs, LSE and mean scores.  Each scored level first scores its candidates from a float16 copy of the
 // summaries (half the bytes of the split rows, half the products) and bounds, per candidate, how
 // far route_kernel's score from the split rows can lie from that estimate.  Only candidates whose
 // interval straddles the K-th place are scored again from the split rows, with route_kernel's
@@ -340,6 +340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 //    its score from the (R, X) of its two children alone.  The rounding differences of the logit
 //    scaling, the exp2/log2 evaluation and the head sum are at most 2^-20 (|z0| + |z1| + 1) per
 //    head, with |z_i| <= c2 (|q_h| + |eps_h|) X_i (1 + g);
+//  * the mean of two logits (PISA-1) also moves by at most the larger change.  (The mean + var/2
+//    variant keeps route_kernel: the bound of its half variance re-scored most candidates, slower);
 //  * with L = u - E and U = u + E around the estimate u: a candidate whose L exceeds the (K+1)-th
 //    largest U is in the split score's top K, one whose U is below the K-th largest L is not, and the
 //    rest are scored again and fill the remaining places by (score, then lower index).  Should the
@@ -366,7 +368,7 @@ struct F16Tile {                                     // the float16 copy of 16 c
   }
 };
 
-template <int D>
+template <int D, int kScore>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void route_prefilter_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = blockIdx.x * 4 + wave;
@@ -412,6 +414,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   const float qn_sum = row_sum_to_last(head_ok ? qn : 0.f), qd_sum = row_sum_to_last(head_ok ? qd : 0.f);
   const float QN = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qn_sum), 15)) * 1.000001f;
   const float QD = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qd_sum), 15)) * 1.000001f;
+  static_assert(kScore == 0 || kScore == 1, "the pre-filter serves the LSE and mean scores");
+  const float cs = kScore == 0 ? c2 : a.scale;        // score units per logit: base 2 (LSE) or natural
   const uint16_t* rows = a.split + (int64_t)bh * a.pairs * (4 * D);
   const uint16_t* rows16 = a.split16 + (int64_t)bh * a.pairs * (2 * D);
   const float4* bounds = reinterpret_cast<const float4*>(a.bounds) + (int64_t)bh * a.pairs;
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         float ps[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, 0, a.scale, c2);
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, kScore, a.scale, c2);
           ps[h] = row_sum_to_last(head_ok ? sc : 0.f);
         }
         const int src = 16 * ((lane & 7) >> 1) + 15;
@@ -467,9 +471,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       // E: the sum over heads of c2 max_i (|q_h| R_i + |eps_h| X_i (1 + 2^-15) + 2^-24 |y_i|) (1 + 2^-23),
       // with |y_i| <= (|q_h| + |eps_h|) X_i (1 + g), plus the rounding slack 2^-20 (|z0| + |z1| + 1)
       // per head, here doubled
+      // (c2 in base-2 units for the LSE, the scale for the mean variants; the mean of two logits moves by
+      // at most their larger change, like the LSE)
       const float rmax = fmaxf(b4.x, b4.z), xmax = fmaxf(b4.y, b4.w);
-      const float E = c2 * 1.001f * (rmax * QN + xmax * (QD * 1.0001f + 0x1p-23f * (QN + QD))) +
-                      0x1p-19f * (c2 * (QN + QD) * (b4.y + b4.w) * 1.001f + (float)a.group) + 0x1p-40f;
+      const float dsum = rmax * QN + xmax * (QD * 1.0001f + 0x1p-23f * (QN + QD));
+      const float E = cs * 1.001f * dsum + 0x1p-19f * (cs * (QN + QD) * (b4.y + b4.w) * 1.001f + (float)a.group) +
+                      0x1p-40f;
       // the interval [u - E', u + E'] holds route_kernel's score (E' also covers rounding here)
       const bool vc = cand >= 0;
       const float Ep = E * 1.0000003f + 0x1p-20f * fabsf(u) + 0x1p-40f;
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
             float pscore[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, 0,
+              const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, kScore,
                                           a.scale, c2);
               pscore[h] = row_sum_to_last(head_ok ? sc : 0.f);
             }
@@ -539,8 +546,11 @@ template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
   if constexpr (sizeof(T) == 2) {
-    if (a.prefilter && a.score == 0) {
-      hipLaunchKernelGGL(route_prefilter_kernel<D>, grid, dim3(256), 0, s, a);
+    if (a.prefilter && a.score != 2) {
+      if (a.score == 1)
+        hipLaunchKernelGGL((route_prefilter_kernel<D, 1>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((route_prefilter_kernel<D, 0>), grid, dim3(256), 0, s, a);
       return launched(s);
     }
   }

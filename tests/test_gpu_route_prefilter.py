@@ -1,4 +1,5 @@
-"""Routing with the high-part pre-filter (the default for bf16 inputs with the LSE score) keeps exactly
+"""Routing with the float16 pre-filter (the default for bf16 inputs with the LSE and mean scores; the
+mean + var/2 score always takes the exact path and is compared as a control) keeps exactly
 the candidates that routing keeps when it scores every candidate from the full split rows
 (PISA_ROUTE_EXACT=1 in the environment).  A child process with the variable set routes the same
 inputs; the leaf candidates that routing leaves in the workspace and the final selections must agree
@@ -67,19 +68,32 @@ def draw(case):
     return q.to(torch.bfloat16), k.to(torch.bfloat16)
 
 
+# the score variants (PISA-1 / PISA-2) on a subset of the cases
+VARIANT_CASES = (1, 4, 7, 8, 9, 10)
+
+
+def runs():
+    for i in range(len(CASES)):
+        yield i, "lse"
+    for i in VARIANT_CASES:
+        for score in ("mean", "mean_var"):
+            yield i, score
+
+
 def run_all() -> dict:
     out = {}
-    for i, case in enumerate(CASES):
+    for i, score in runs():
+        case = CASES[i]
         B, N, Hq, Hkv, d, K = case[:6]
         q, k = draw(case)
         pyr = binding.build_pyramid(k)
         cfg = binding.make_cfg(B, N, Hq, Hkv, d, K, q.dtype)
         ws = torch.empty(binding.select_workspace_bytes(cfg), dtype=torch.uint8, device=H.DEV)
-        sel = binding.select_blocks(q, k, pyr, K, workspace=ws)
+        sel = binding.select_blocks(q, k, pyr, K, workspace=ws, score=score)
         torch.cuda.synchronize()
         slots = B * Hkv * N * 2 * K
-        out[f"cand{i}"] = ws[:slots * 4].view(torch.int32).cpu().numpy()
-        out[f"sel{i}"] = sel.cpu().numpy()
+        out[f"cand{i}_{score}"] = ws[:slots * 4].view(torch.int32).cpu().numpy()
+        out[f"sel{i}_{score}"] = sel.cpu().numpy()
         del q, k, pyr, ws, sel
         torch.cuda.empty_cache()
     return out
@@ -99,8 +113,9 @@ def test_prefilter_keeps_what_exact_routing_keeps(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     there = np.load(out)
-    for i, case in enumerate(CASES):
-        for name in (f"cand{i}", f"sel{i}"):
+    for i, score in runs():
+        case = CASES[i]
+        for name in (f"cand{i}_{score}", f"sel{i}_{score}"):
             diff = int((here[name] != there[name]).sum())
-            H.log(f"[route pre-filter] case {case[:6]} {case[9]} {name[:-len(str(i))]}: {diff} differing entries")
-            assert diff == 0, (case, name)
+            H.log(f"[route pre-filter] case {case[:6]} {case[9]} {score} {name.split(str(i))[0]}: {diff} differing entries")
+            assert diff == 0, (case, score, name)
