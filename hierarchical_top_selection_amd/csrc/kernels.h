@@ -47,7 +47,7 @@ struct RouteArgs {
   int score;          // 0 LSE, 1 mean, 2 mean + var / 2 (pisa_score)
   float scale;
   bool bf16;
-  bool prefilter;     // bf16 routing, LSE and mean scores: the float16 copy first (route_prefilter_kernel)
+  bool prefilter;     // bf16 routing: score from the float16 copy first (route_prefilter_kernel)
   Levels lv;
 };
 

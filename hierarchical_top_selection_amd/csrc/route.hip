@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 }
 
 // ----------------------------------------------------------------------------- routing with a pre-filter
-// bf16 inputs, LSE and mean scores.  Each scored level first scores its candidates from a float16 copy of the
+// bf16 inputs, every score.  Each scored level first scores its candidates from a float16 copy of the
 // summaries (half the bytes of the split rows, half the products) and bounds, per candidate, how
 // far route_kernel's score from the split rows can lie from that estimate.  Only candidates whose
 // interval straddles the K-th place are scored again from the split rows, with route_kernel's
@@ -340,8 +340,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 //    its score from the (R, X) of its two children alone.  The rounding differences of the logit
 //    scaling, the exp2/log2 evaluation and the head sum are at most 2^-20 (|z0| + |z1| + 1) per
 //    head, with |z_i| <= c2 (|q_h| + |eps_h|) X_i (1 + g);
-//  * the mean of two logits (PISA-1) also moves by at most the larger change.  (The mean + var/2
-//    variant keeps route_kernel: the bound of its half variance re-scored most candidates, slower);
+//  * the mean of two logits (PISA-1) also moves by at most the larger change; the added half variance
+//    (PISA-2) h^2 / 2 with h = (a - b) / 2 by at most |h| |dh| + dh^2 / 2 with |dh| <= scale max_i |dy_i|,
+//    which needs the sums over heads of |q_h| |h_h| and |eps_h| |h_h| per candidate (two more head
+//    sums in the tile loop), and its rounding 2^-21 h^2 per head more, h^2 <= (scale (|q_h| +
+//    |eps_h|) (X0 + X1) / 2)^2;
 //  * with L = u - E and U = u + E around the estimate u: a candidate whose L exceeds the (K+1)-th
 //    largest U is in the split score's top K, one whose U is below the K-th largest L is not, and the
 //    rest are scored again and fill the remaining places by (score, then lower index).  Should the
@@ -414,8 +417,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   const float qn_sum = row_sum_to_last(head_ok ? qn : 0.f), qd_sum = row_sum_to_last(head_ok ? qd : 0.f);
   const float QN = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qn_sum), 15)) * 1.000001f;
   const float QD = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qd_sum), 15)) * 1.000001f;
-  static_assert(kScore == 0 || kScore == 1, "the pre-filter serves the LSE and mean scores");
   const float cs = kScore == 0 ? c2 : a.scale;        // score units per logit: base 2 (LSE) or natural
+  float Q2 = 0.f;                                      // mean + var / 2: sum over heads of (|q_h| + |eps_h|)^2
+  if constexpr (kScore == 2) {
+    const float q2_sum = row_sum_to_last(head_ok ? (qn + qd) * (qn + qd) : 0.f);
+    Q2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q2_sum), 15)) * 1.000001f;
+  }
   const uint16_t* rows = a.split + (int64_t)bh * a.pairs * (4 * D);
   const uint16_t* rows16 = a.split16 + (int64_t)bh * a.pairs * (2 * D);
   const float4* bounds = reinterpret_cast<const float4*>(a.bounds) + (int64_t)bh * a.pairs;
@@ -444,6 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       // (R0, X0, R1, X1) of this lane's candidate's two children, for its bound after the tiles
       const float4 b4 = bounds[a.pair_off[level - 2] + (cand >= 0 ? cand : 0)];
       float u = kNegInf;                               // estimate of candidate `lane`
+      float hq = 0.f, he = 0.f;                        // mean + var / 2: sums over heads of |q_h| |h_h|, |eps_h| |h_h|
       auto do_tile = [&](int nt, F16Tile<D>& cur, F16Tile<D>& nxt, bool& ok_cur) {
         const uint32_t rows_ok = (uint32_t)__ballot(ok_cur) >> (4 * g);
         bool ok_n;
@@ -451,15 +459,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         nxt.load(a, rows16, level - 2, child_n, g);
         ok_cur = ok_n;
         const floatx4 acc = mma(cur.f, qf.l, floatx4{0.f, 0.f, 0.f, 0.f});
-        float ps[2];
+        float ps[2], pq[2], pe[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, (rows_ok >> (2 * h + 1)) & 1u, kScore, a.scale, c2);
+          const bool ok1 = (rows_ok >> (2 * h + 1)) & 1u;
+          const float sc = pair_score(acc[2 * h], acc[2 * h + 1], true, ok1, kScore, a.scale, c2);
           ps[h] = row_sum_to_last(head_ok ? sc : 0.f);
+          if constexpr (kScore == 2) {
+            const float hh = head_ok && ok1 ? 0.5f * fabsf(acc[2 * h] - acc[2 * h + 1]) * a.scale : 0.f;
+            pq[h] = row_sum_to_last(qn * hh);
+            pe[h] = row_sum_to_last(qd * hh);
+          }
         }
         const int src = 16 * ((lane & 7) >> 1) + 15;
         const float s0 = __shfl(ps[0], src, 64), s1 = __shfl(ps[1], src, 64);
         if ((lane >> 3) == nt) u = (lane & 1) ? s1 : s0;
+        if constexpr (kScore == 2) {
+          const float q0 = __shfl(pq[0], src, 64), q1 = __shfl(pq[1], src, 64);
+          const float e0 = __shfl(pe[0], src, 64), e1 = __shfl(pe[1], src, 64);
+          if ((lane >> 3) == nt) {
+            hq = (lane & 1) ? q1 : q0;
+            he = (lane & 1) ? e1 : e0;
+          }
+        }
       };
       bool ok_t;
       F16Tile<D> ta, tb;
@@ -475,8 +497,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       // at most their larger change, like the LSE)
       const float rmax = fmaxf(b4.x, b4.z), xmax = fmaxf(b4.y, b4.w);
       const float dsum = rmax * QN + xmax * (QD * 1.0001f + 0x1p-23f * (QN + QD));
-      const float E = cs * 1.001f * dsum + 0x1p-19f * (cs * (QN + QD) * (b4.y + b4.w) * 1.001f + (float)a.group) +
-                      0x1p-40f;
+      float E = cs * 1.001f * dsum + 0x1p-19f * (cs * (QN + QD) * (b4.y + b4.w) * 1.001f + (float)a.group) + 0x1p-40f;
+      if constexpr (kScore == 2) {
+        // sum over heads of |h| |dh| <= scale (R_max hq + X_max (1 + 2^-13) he + 2^-23 (X0 + X1) (hq + he)),
+        // of dh^2 / 2 <= (scale dsum)^2 / 2; the rounding of h^2 / 2
+        const float sx = a.scale * (b4.y + b4.w);
+        E += a.scale * 1.001f * (rmax * hq + xmax * 1.0002f * he + 0x1p-23f * (b4.y + b4.w) * (hq + he)) +
+             0.5f * (cs * 1.001f * dsum) * (cs * 1.001f * dsum) + 0x1p-19f * 0.25f * sx * sx * Q2;
+      }
       // the interval [u - E', u + E'] holds route_kernel's score (E' also covers rounding here)
       const bool vc = cand >= 0;
       const float Ep = E * 1.0000003f + 0x1p-20f * fabsf(u) + 0x1p-40f;
@@ -546,9 +574,11 @@ template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   dim3 grid(ceil_div(a.n, 4), a.batch * a.n_kv_heads);
   if constexpr (sizeof(T) == 2) {
-    if (a.prefilter && a.score != 2) {
+    if (a.prefilter) {
       if (a.score == 1)
         hipLaunchKernelGGL((route_prefilter_kernel<D, 1>), grid, dim3(256), 0, s, a);
+      else if (a.score == 2)
+        hipLaunchKernelGGL((route_prefilter_kernel<D, 2>), grid, dim3(256), 0, s, a);
       else
         hipLaunchKernelGGL((route_prefilter_kernel<D, 0>), grid, dim3(256), 0, s, a);
       return launched(s);

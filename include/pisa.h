@@ -167,7 +167,7 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  * inputs the float32 summaries above the leaves enter the dot products as a
  * bf16 part plus a float16 remainder scaled by 2^10 (about 2^-20 relative
  * error per element); float32 inputs use the summaries as they are.  With
- * the LSE and mean scores, bf16 routing first scores each level from a float16 copy of
+ * every score, bf16 routing first scores each level from a float16 copy of
  * the summaries with a bound on its distance to the split score, and scores
  * again from both split parts only the candidates the bound leaves
  * undecided; the kept sets are those of scoring every candidate from both

@@ -1,5 +1,4 @@
-"""Routing with the float16 pre-filter (the default for bf16 inputs with the LSE and mean scores; the
-mean + var/2 score always takes the exact path and is compared as a control) keeps exactly
+"""Routing with the float16 pre-filter (the default for bf16 inputs, every score) keeps exactly
 the candidates that routing keeps when it scores every candidate from the full split rows
 (PISA_ROUTE_EXACT=1 in the environment).  A child process with the variable set routes the same
 inputs; the leaf candidates that routing leaves in the workspace and the final selections must agree
