@@ -54,20 +54,36 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
         for (int r = 0; r < 4; ++r)
           if (key_off(mt, r) > lim) acc[mt][r] = kNegInf;
     }
-    float m = kNegInf;
+    // First with no shift: s = sum of 2^(x c2).  When every head's s lies in [2^-60, 2^60], its
+    // largest term lies in [2^-66, 2^60]: no term overflowed, the terms that underflowed (below
+    // 2^-126) are below 2^-60 of the largest, and log2 s is the base-2 LSE to the rounding of the max-shifted form
+    // (whose shift m c2 is rounded the same way as x c2 here).  Otherwise the whole wave redoes the
+    // pair with the maximum subtracted first.
+    float s = __builtin_amdgcn_exp2f(acc[0][0] * c2);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][r]);
-    m = rows_max(m);
-    const float mc = m * c2;
-    float s = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
+      for (int r = 0; r < 4; ++r)
+        if (mt + r > 0) s += __builtin_amdgcn_exp2f(acc[mt][r] * c2);
     s = rows_sum(s);
-    // natural-log LSE: (m c2 + log2 s) ln 2; s >= 1, so the raw log2 needs no fix-up
+    float mc = 0.f;
+    if (__ballot(!(s >= 0x1p-60f && s <= 0x1p60f))) {   // wave-uniform
+      float m = kNegInf;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][r]);
+      m = rows_max(m);
+      mc = m * c2;
+      s = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][r], c2, -mc));   // arguments <= 0
+      s = rows_sum(s);
+    }
+    // natural-log LSE: (m c2 + log2 s) ln 2; s >= 2^-60 (>= 1 after the shift), so the raw log2
+    // needs no fix-up for denormals
     head = (mc + __builtin_amdgcn_logf(s)) * 0.6931471805599453f;
   } else {                                              // mean, or mean + var / 2, of the valid logits
     const float cnt = (float)(min(lim, kLeaf - 1) + 1);

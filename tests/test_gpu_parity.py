@@ -25,10 +25,13 @@ def _pyramid_levels(flat: np.ndarray, n: int, capacity: int):
     return out
 
 
-def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: int = 0):
+def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: int = 0, inputs=None,
+                  attn_abs: float | None = None):
+    """inputs: (q, k, v) storage arrays to use instead of the workload's own draw; attn_abs: a
+    max-abs gate for the attention outputs in place of the workload's."""
     B, N, G, K = w.batch, w.seq_len, w.group, w.top_k
     H.log(f"[{label}] inputs B={B} N={N} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} K={K} {w.dtype}")
-    q, k, v = W.prefill_inputs(w, bits=True)
+    q, k, v = W.prefill_inputs(w, bits=True) if inputs is None else inputs
     H.log(f"[{label}] GPU pyramid + select + attention")
     g = H.run_gpu_prefill(w, q, k, v)
     pyr = g["pyr"].cpu().numpy()
@@ -66,10 +69,11 @@ def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: in
             # end-to-end attention where the selections agree
             heads = slice(kvh * G, (kvh + 1) * G)
             tol_abs, tol_rel = H.attn_tolerance(w)
+            tol_abs = tol_abs if attn_abs is None else attn_abs
             ma, rl = H.attn_errors(o[b, ts][:, heads][agree], ora["o"][agree])
             assert ma <= tol_abs and rl <= tol_rel, (label, "end-to-end", ma, rl)
             if w.dtype == "bf16":
-                H.assert_bf16_output(o_native[b, ts][:, heads][agree], ora["o"][agree], label)
+                H.assert_bf16_output(o_native[b, ts][:, heads][agree], ora["o"][agree], label, abs_gate=tol_abs)
             sel_in[b, kvh, torch.from_numpy(ts).to(H.DEV)] = torch.from_numpy(ora["sel"].astype(np.int32)).to(H.DEV)
             units.append((b, kvh, ts, ora))
     H.assert_mismatch_budget(n_bad, n_total, label)
@@ -84,6 +88,7 @@ def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: in
         ma, rl = H.attn_errors(o2[b, ts][:, heads], ora["o"])
         worst = (max(worst[0], ma), max(worst[1], rl))
         tol_abs, tol_rel = H.attn_tolerance(w)
+        tol_abs = tol_abs if attn_abs is None else attn_abs
         assert ma <= tol_abs and rl <= tol_rel, (label, b, kvh, ma, rl)
         np.testing.assert_allclose(lse2[b, heads][:, ts].T, ora["lse"], atol=2e-4 if w.dtype == "bf16" else 2e-5)
     H.log(f"[{label}] attention on oracle selection: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
@@ -118,6 +123,63 @@ def test_prefill_shapes(d, hq, hkv, K, n, dtype):
 def test_prefill_tiny_lengths(n):
     w = W.WORKLOADS["prefill_n4096"].with_(name="short", seq_len=n, top_k=2, n_q_heads=4, seed=30 + n)
     check_prefill(w, f"short_n{n}")
+
+
+def _leaf_sums_log2(q: np.ndarray, k: np.ndarray, G: int, scale: float) -> np.ndarray:
+    """log2 of sum_k 2^(q_h . k c2) over each causal leaf of each token's first KV head (fp64), for
+    every head: [N, M1, G]; -inf where the leaf starts after the token."""
+    N = q.shape[1]
+    m1 = -(-N // 64)
+    qq = H.host_values(q[0, :, :G]).astype(np.float64)            # [N, G, d]
+    kk = H.host_values(k[0, :, 0]).astype(np.float64)             # [N, d]
+    y = np.einsum("tgd,sd->tgs", qq, kk) * scale * np.log2(np.e)  # [N, G, N]
+    y = np.where(np.arange(N)[None, None, :] <= np.arange(N)[:, None, None], y, -np.inf)
+    out = np.full((N, m1, G), -np.inf)
+    for j in range(m1):
+        blk = y[:, :, 64 * j:64 * j + 64]
+        m = blk.max(-1)
+        with np.errstate(invalid="ignore"):
+            out[:, j] = m + np.log2(np.exp2(blk - m[..., None]).sum(-1))
+    return out
+
+
+@pytest.mark.parametrize("regime", ["wide", "large", "negative"])
+def test_prefill_logit_ranges(regime):
+    """Stage 2 sums 2^(scaled logit) with no shift while every head's sum lies in [2^-60, 2^60] and
+    takes the max-shifted sum otherwise.  Inputs whose leaf sums fall on both sides of that range
+    ("wide": queries and keys scaled by 4), above it everywhere ("large": by 8) and below it
+    ("negative": keys along +u, queries along -u, so every logit is far below zero) must still match
+    the oracle: selections by the boundary rule, leaf scores and outputs.
+
+    With logits this far apart a row's softmax sits on one or two keys, so the rounding of P to
+    bf16 before the P V product (at most 2^-8 of each weight) no longer averages out: the output
+    can be off by up to 2^-8 max |v|, which is the max-abs gate here (plus 1e-3 for the fp32 sums);
+    the relative-L2 gate is the workload's."""
+    w = W.WORKLOADS["prefill_n4096"].with_(name=f"range_{regime}", seq_len=1500, batch=1, n_q_heads=8,
+                                           n_kv_heads=1, top_k=4, seed=41)
+    q, k, v = W.prefill_inputs(w)                                  # float32 values
+    d = w.head_dim
+    if regime == "wide":
+        q, k = q * 4.0, k * 4.0
+    elif regime == "large":
+        q, k = q * 8.0, k * 8.0
+    else:
+        u = np.random.default_rng(42).standard_normal(d)
+        u /= np.linalg.norm(u)
+        q = q - 40.0 * u
+        k = k + 40.0 * u
+    q, k, v = (W.to_storage(x.astype(np.float32), "bf16") for x in (q, k, v))
+    s2 = _leaf_sums_log2(q, k, w.group, 1.0 / np.sqrt(d))
+    causal = np.isfinite(s2)
+    outside = causal & ((s2 < -60) | (s2 > 60))
+    frac = outside.sum() / causal.sum()
+    H.log(f"[range {regime}] {frac:.3f} of (token, leaf, head) sums outside [2^-60, 2^60]")
+    if regime == "wide":
+        assert 0.01 < frac < 0.99
+    else:
+        assert frac > 0.99
+    vmax = float(np.abs(H.host_values(v)).max())
+    check_prefill(w, f"range_{regime}", inputs=(q, k, v), attn_abs=vmax / 256.0 + 1e-3)
 
 
 def test_all_leaves_selected_is_dense_causal_attention():
