@@ -275,26 +275,41 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) sel[h][e] = (__bf16)(8 * g + e == 16 * h + col ? 1.f : 0.f);
   const int my_sel = lane < a.top_k ? a.sel[((int64_t)bh * a.n + t) * a.top_k + lane] : -1;
   uint64_t rest = __ballot(slot_in_use(my_sel, lane, a.top_k, t));
+  const int nsel = __popcll(rest);
 
   floatx4 dq[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) dq[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  while (rest) {
-    const int leaf = __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64));
+  // K one block ahead: the next block's K is requested half by half, as soon as the dq products have
+  // read each half of this block's K.
+  Frag kf[4];
+  auto load_k = [&](int leaf, int m0) {
+    const int64_t off = (int64_t)leaf * (kLeaf * D / 8);
+#pragma unroll
+    for (int mt = m0; mt < m0 + 2; ++mt)
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) kf[mt].v[s] = krow[off + (mt * (D / 32) + s) * 64];
+  };
+  int leaf = 0;
+  if (rest) {
+    leaf = __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64));
+    rest &= rest - 1;
+    load_k(leaf, 0);
+    load_k(leaf, 2);
+  }
+  for (int done = 0; done < nsel; ++done) {
+    const bool more = rest != 0;
+    const int leaf_n = more ? __builtin_amdgcn_readfirstlane(__shfl(my_sel, __builtin_ctzll(rest), 64)) : 0;
     rest &= rest - 1;
     const int64_t first = (int64_t)leaf * kLeaf;
     const int64_t off = (int64_t)leaf * (kLeaf * D / 8);
     floatx4 s_acc[4], p_acc[4];
-    Frag kf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       Frag vf;
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        kf[mt].v[s] = krow[off + (mt * (D / 32) + s) * 64];
-        vf.v[s] = vrow[off + (mt * (D / 32) + s) * 64];
-      }
+      for (int s = 0; s < D / 32; ++s) vf.v[s] = vrow[off + (mt * (D / 32) + s) * 64];
       s_acc[mt] = mma(kf[mt], qf, floatx4{0.f, 0.f, 0.f, 0.f});
       p_acc[mt] = mma(vf, df, floatx4{0.f, 0.f, 0.f, 0.f});
     }
@@ -311,11 +326,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         db[mt >> 1][4 * (mt & 1) + r] = (__bf16)(p * (p_acc[mt][r] - st.y));
       }
     // dq^T += K^T dS^T.  The A fragment of key half kb and d tile dt holds, in lane (g, col), element
-    // e: K[first + perm_key(2 kb + e / 4, 4 g + e % 4)][16 dt + col], the key order of db[kb].
+    // e: K[first + perm_key(2 kb + e / 4, 4 g + e % 4)][16 dt + col], the key order of db[kb].  Each
+    // dq[dt] still takes key half 0, then key half 1.
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int dt = 0; dt < D / 16; ++dt) {
         const floatx4 lo = mfma_bf16(kf[2 * kb].v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
         const floatx4 hi = mfma_bf16(kf[2 * kb + 1].v[dt >> 1], sel[dt & 1], floatx4{0.f, 0.f, 0.f, 0.f});
         bf16x8 kt;
@@ -326,7 +342,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         }
         dq[dt] = mfma_bf16(kt, db[kb], dq[dt]);
       }
+      if (more) load_k(leaf_n, 2 * kb);
     }
+    leaf = leaf_n;
   }
   if (col < a.group) {
     float* out = a.dq + b * a.dq_sb + (int64_t)t * a.dq_st + (int64_t)head * a.dq_sh;
