@@ -253,32 +253,10 @@ def run_workload(w: W.Workload, steps: int, warmup: int) -> dict:
             "leaf_flops": leaf_flops, "kernel_names": names, "kernel_ms": kernel_ms}
 
 
-def device_inputs(w: W.Workload, n: int, seed: int = 7):
-    """Q and K of n tokens drawn on the device with the workload's recipe (N(0,1), queries + alpha_q u,
-    keys of round(frac * M1) random leaf blocks + alpha_k u, the same fraction of planted blocks as w),
-    rounded to bf16; for lengths whose host draw would take minutes."""
-    import torch
-
-    gen = torch.Generator(device="cuda:0")
-    gen.manual_seed(seed)
-    d = w.head_dim
-    u = torch.randn(d, generator=gen, device="cuda:0")
-    u = u / u.norm()
-    q = torch.randn((w.batch, n, w.n_q_heads, d), generator=gen, device="cuda:0") + w.alpha_q * u
-    k = torch.randn((w.batch, n, w.n_kv_heads, d), generator=gen, device="cuda:0")
-    m1 = -(-n // 64)
-    n_plant = max(1, round(w.plant_blocks / w.n_leaves * m1))
-    for b in range(w.batch):
-        for h in range(w.n_kv_heads):
-            for j in torch.randperm(m1, generator=gen, device="cuda:0")[:n_plant].tolist():
-                k[b, 64 * j:64 * j + 64, h] += w.alpha_k * u
-    return q.to(torch.bfloat16), k.to(torch.bfloat16)
-
-
 def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5, w: W.Workload | None = None,
                     longer=(524288, 1000000)) -> dict:
     """Selection latency, hierarchical vs single-level, on prefixes N = 4K .. full of one input,
-    then at the `longer` lengths on device-drawn inputs of the same recipe (`device_inputs`).
+    then at the `longer` lengths on device-drawn inputs of the same recipe (`W.device_prefill_inputs`).
 
     Both sides build the key pyramid (the flat scan reads its leaf means) and then
     select K leaves per token: `select_blocks` (routing + exact leaf LSE + top-K)
@@ -296,7 +274,7 @@ def selection_sweep(q, k, n_kv_heads: int, K: int = 8, reps: int = 5, w: W.Workl
            "pisa_select_ms": [], "flat_select_ms": [], "flat_over_pisa": []}
     for n in ns + longer:
         if n in longer:
-            qn, kn = device_inputs(w, n)
+            qn, kn = W.device_prefill_inputs(w, n)
         else:
             qn, kn = q[:, :n], k[:, :n]
         cfg = binding.make_cfg(B, n, Hq, n_kv_heads, d, K, q.dtype)

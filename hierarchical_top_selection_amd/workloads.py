@@ -197,6 +197,37 @@ def v_slice(w: Workload, b: int, kvh: int, n: int | None = None) -> np.ndarray:
     return draw(w, "v", b, kvh, n)
 
 
+def device_prefill_inputs(w: Workload, n: int, seed: int = 7, with_v: bool = False):
+    """Q and K (and V) of n tokens drawn on the GPU, for lengths whose host draw would take minutes.
+
+    The recipe of the host draw with torch's generator instead of NumPy's streams (so the values
+    differ from ``prefill_inputs``): u = a normalised N(0,1) vector, Q = N(0,1) + alpha_q u,
+    K = N(0,1) with alpha_k u added to every key of round(frac * M1) leaf blocks chosen by a
+    random permutation (frac = the workload's planted fraction), V = N(0,1); all drawn in float32
+    from one generator seeded with ``seed``, in that order, then rounded to bf16.
+    """
+    import torch
+
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(seed)
+    d = w.head_dim
+    u = torch.randn(d, generator=gen, device="cuda:0")
+    u = u / u.norm()
+    q = torch.randn((w.batch, n, w.n_q_heads, d), generator=gen, device="cuda:0") + w.alpha_q * u
+    k = torch.randn((w.batch, n, w.n_kv_heads, d), generator=gen, device="cuda:0")
+    m1 = -(-n // w.block)
+    n_plant = max(1, round(w.plant_blocks / w.n_leaves * m1))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            for j in torch.randperm(m1, generator=gen, device="cuda:0")[:n_plant].tolist():
+                k[b, w.block * j:w.block * (j + 1), h] += w.alpha_k * u
+    out = [q.to(torch.bfloat16), k.to(torch.bfloat16)]
+    del q, k
+    if with_v:
+        out.append(torch.randn((w.batch, n, w.n_kv_heads, d), generator=gen, device="cuda:0").to(torch.bfloat16))
+    return tuple(out)
+
+
 def decode_tokens(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     """New per-step vectors [steps, d] for 'q', 'k' or 'v' of sequence b, head h."""
     tid = {"q": 10, "k": 11, "v": 12}[which]

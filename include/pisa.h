@@ -183,6 +183,8 @@ size_t pisa_select_workspace_bytes(const pisa_cfg* cfg);
  *             about the size of q plus k); its first
  *             B*H_kv*N*2K int32 hold the leaf candidates of each token (-1
  *             padded) after the call
+ * Returns PISA_ERR_UNSUPPORTED for N > 1000000 (the leaf clustering keeps a
+ * counter per leaf block of the sequence in LDS).
  */
 pisa_status pisa_select_blocks(const pisa_cfg* cfg, pisa_tensor q, pisa_tensor k, const float* pyr,
                                int32_t* sel, float* sel_u, void* ws, size_t ws_bytes, void* stream);
