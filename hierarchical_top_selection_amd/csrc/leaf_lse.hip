@@ -113,10 +113,14 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
 }
 
 // Each wave walks kItemsPerWave consecutive items of one window as one stream of pairs:
-// the query rows are fetched two pairs ahead (across item boundaries), and consecutive
-// items of the same leaf keep their keys.
+// the query rows are fetched kAhead pairs ahead (across item boundaries), and consecutive
+// items of the same leaf keep their keys.  Two pairs ahead at three waves per SIMD suits the
+// 1024-token windows of long sequences, whose query rows often come from beyond the L2; one
+// pair ahead at four waves per SIMD (128 VGPRs) the 512-token windows, whose rows mostly hit
+// it (measured: 2.46 -> 2.34 ms at 32K, 3.37 -> 3.49 ms at 256K).
 // fp32 keys at d = 128 need 128 VGPRs of fragments: no occupancy target there.
-template <typename T, int D, int kScore, int kWaves = (sizeof(T) == 4 && D == 128) ? 1 : 3>
+template <typename T, int D, int kScore, int kAhead,
+          int kWaves = (sizeof(T) == 4 && D == 128) ? 1 : (kAhead == 2 ? 3 : 4)>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) void leaf_lse_kernel(LeafArgs a) {
   typedef typename RawFrag<T, D>::type Frag;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -206,17 +210,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves))) v
       ++next_item;
       next_start = __builtin_amdgcn_readfirstlane(next_item < nit ? pick(next_item, 0, off1, off2, off3) : total);
     }
-    load_q(fill, pair_at(min(f + 2, total - 1)));     // past the end: a repeat, never used
+    load_q(fill, pair_at(min(f + kAhead, total - 1)));   // past the end: a repeat, never used
     leaf_pair<T, D, kScore>(kf, cur, pair_at(f), a, start, last, c2, head_ok, g, lane, uout);
   };
-  Frag qa, qb, qc;
-  load_q(qa, pair_at(0));
-  load_q(qb, pair_at(min(1, total - 1)));
-  for (int f = 0; f < total; f += 3) {
-    step(f, qa, qc);
-    if (f + 1 < total) step(f + 1, qb, qa);
-    if (f + 2 < total) step(f + 2, qc, qb);
+  if constexpr (kAhead == 2) {
+    Frag qa, qb, qc;
+    load_q(qa, pair_at(0));
+    load_q(qb, pair_at(min(1, total - 1)));
+    for (int f = 0; f < total; f += 3) {
+      step(f, qa, qc);
+      if (f + 1 < total) step(f + 1, qb, qa);
+      if (f + 2 < total) step(f + 2, qc, qb);
+    }
+  } else {
+    Frag qa, qb;
+    load_q(qa, pair_at(0));
+    for (int f = 0; f < total; f += 2) {
+      step(f, qa, qb);
+      if (f + 1 < total) step(f + 1, qb, qa);
+    }
   }
+}
+
+template <typename T, int D, int kAhead>
+void launch_leaf_score(const LeafArgs& a, dim3 grid, hipStream_t s) {
+  if (a.score == 1)
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 1, kAhead>), grid, dim3(256), 0, s, a);
+  else if (a.score == 2)
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 2, kAhead>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 0, kAhead>), grid, dim3(256), 0, s, a);
 }
 
 template <typename T, int D>
@@ -224,12 +247,10 @@ hipError_t launch_leaf_t(const LeafArgs& a, hipStream_t s) {
   const int64_t windows = (int64_t)a.batch * a.n_kv_heads * a.n_windows;
   const int64_t blocks = kXcds * ((windows + kXcds - 1) / kXcds) * ceil_div(a.item_cap, 4 * kItemsPerWave);
   const dim3 grid((unsigned)blocks);
-  if (a.score == 1)
-    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 1>), grid, dim3(256), 0, s, a);
-  else if (a.score == 2)
-    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 2>), grid, dim3(256), 0, s, a);
+  if (a.window > 512)
+    launch_leaf_score<T, D, 2>(a, grid, s);
   else
-    hipLaunchKernelGGL((leaf_lse_kernel<T, D, 0>), grid, dim3(256), 0, s, a);
+    launch_leaf_score<T, D, 1>(a, grid, s);
   return launched(s);
 }
 
