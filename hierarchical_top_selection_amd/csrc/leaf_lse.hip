@@ -9,8 +9,9 @@
 // bf16 inputs read both from packed copies (K blocks with keys in perm_key order,
 // query groups; pack.hip) so every fragment load is one contiguous run.  The product is kept transposed, S^T = K Q^T
 // (keys on rows, heads on columns), so a lane owns 16 keys of one head: the
-// per-head max and sum over the 64 keys are in-lane plus two row-swap
-// permutes across the lane groups, and exp2/log2 run on pre-scaled logits.  The group's head sum is a
+// per-head sum over the 64 keys (and the maximum, where the sum needs a shift) is
+// in-lane plus two row-swap permutes across the lane groups, and exp2/log2 run on
+// pre-scaled logits.  The group's head sum is a
 // 16-lane reduction; one lane writes the pair's score.  The mean and mean + var/2 score
 // variants (PISA-1 / PISA-2) reduce the same logits to their mean and variance instead; the
 // score is a template parameter, so each instantiation carries only its own reduction.  bf16 inputs use
