@@ -26,9 +26,10 @@ def _pyramid_levels(flat: np.ndarray, n: int, capacity: int):
 
 
 def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: int = 0, inputs=None,
-                  attn_abs: float | None = None):
+                  attn_abs: float | None = None, counts: list | None = None):
     """inputs: (q, k, v) storage arrays to use instead of the workload's own draw; attn_abs: a
-    max-abs gate for the attention outputs in place of the workload's."""
+    max-abs gate for the attention outputs in place of the workload's; counts: a list that
+    receives (mismatches, queries) instead of this call checking the budget on its own."""
     B, N, G, K = w.batch, w.seq_len, w.group, w.top_k
     H.log(f"[{label}] inputs B={B} N={N} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} K={K} {w.dtype}")
     q, k, v = W.prefill_inputs(w, bits=True) if inputs is None else inputs
@@ -76,7 +77,10 @@ def check_prefill(w: W.Workload, label: str, sample: int | None = None, seed: in
                 H.assert_bf16_output(o_native[b, ts][:, heads][agree], ora["o"][agree], label, abs_gate=tol_abs)
             sel_in[b, kvh, torch.from_numpy(ts).to(H.DEV)] = torch.from_numpy(ora["sel"].astype(np.int32)).to(H.DEV)
             units.append((b, kvh, ts, ora))
-    H.assert_mismatch_budget(n_bad, n_total, label)
+    if counts is None:
+        H.assert_mismatch_budget(n_bad, n_total, label)
+    else:
+        counts.append((n_bad, n_total))
     H.log(f"[{label}] max |du| on selected leaves {max_du:.3g}")
     # attention on the oracle's own selection (fed to the kernel as input)
     o2, lse2 = binding.sparse_attn_fwd(g["q"], g["k"], g["v"], sel_in, return_lse=True, out_dtype=torch.float32)

@@ -1,0 +1,52 @@
+"""GPU parity over seeded random shapes: batch, length (ragged and exact multiples of 64), KV heads,
+group size, head dim, K (up to 32, beyond the number of leaves as well), input dtype and candidate
+score, drawn once from a fixed seed so the list is the same on every run.  Every token of every
+case goes through the oracle comparison of the parity tests (pyramid, selections under the boundary
+rule, leaf scores, attention end to end and on the oracle's own selection; the variant cases compare
+selections and leaf scores), and the boundary mismatches are pooled over all cases against the 0.1%
+budget.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gpu_harness as H
+from hierarchical_top_selection_amd import workloads as W
+from test_gpu_parity import check_prefill
+from test_gpu_variants import check_variant
+
+pytestmark = pytest.mark.gpu
+
+
+def cases(count: int = 48):
+    rng = np.random.default_rng(2024)
+    out = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.choice([int(rng.integers(1, 3000)), 64 * int(rng.integers(1, 45))]))
+        b = int(rng.integers(1, 4)) if n * hkv <= 2000 else 1
+        d = int(rng.choice([64, 128]))
+        k = int(rng.integers(1, 33))
+        dtype = "f32" if i % 6 == 5 else "bf16"
+        score = ("lse", "lse", "mean", "mean_var")[i % 4]
+        out.append(dict(batch=b, seq_len=n, n_kv_heads=hkv, n_q_heads=g * hkv, head_dim=d, top_k=k, dtype=dtype,
+                        seed=300 + i, score=score))
+    return out
+
+
+def test_random_shapes_pooled_budget():
+    counts = []
+    for i, c in enumerate(cases()):
+        score = c.pop("score")
+        w = W.WORKLOADS["prefill_n4096"].with_(name=f"rand{i}", **c)
+        label = (f"rand{i}_b{w.batch}_n{w.seq_len}_hkv{w.n_kv_heads}_g{w.group}_d{w.head_dim}_k{w.top_k}_"
+                 f"{w.dtype}_{score}")
+        if score == "lse":
+            check_prefill(w, label, counts=counts)
+        else:
+            check_variant(w, score, label, counts=counts)
+    n_bad = sum(c[0] for c in counts)
+    n_total = sum(c[1] for c in counts)
+    H.assert_mismatch_budget(n_bad, n_total, "random shapes")

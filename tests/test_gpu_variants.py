@@ -28,7 +28,8 @@ def leaf_score(qg: np.ndarray, keys: np.ndarray, j: int, t: int, score: str) -> 
     return float(oracle.child_score(z, np.ones(z.shape, dtype=bool), score).sum())
 
 
-def check_variant(w: W.Workload, score: str, label: str, sample: int | None = None):
+def check_variant(w: W.Workload, score: str, label: str, sample: int | None = None, counts: list | None = None):
+    """counts: a list that receives (mismatches, queries) instead of this call checking the budget."""
     B, N, G, K = w.batch, w.seq_len, w.group, w.top_k
     H.log(f"[{label}] inputs B={B} N={N} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} K={K} score={score}")
     q, k, _ = W.prefill_inputs(w, bits=True)
@@ -62,7 +63,10 @@ def check_variant(w: W.Workload, score: str, label: str, sample: int | None = No
                     du = abs(float(sel_u[b, kvh, t, slot]) - want)
                     max_du = max(max_du, du)
                     assert du <= 1e-4 + 1e-5 * abs(want), (label, t, j, float(sel_u[b, kvh, t, slot]), want)
-    H.assert_mismatch_budget(n_bad, n_total, label)
+    if counts is None:
+        H.assert_mismatch_budget(n_bad, n_total, label)
+    else:
+        counts.append((n_bad, n_total))
     H.log(f"[{label}] max |du| on selected leaves {max_du:.3g}")
 
 
