@@ -1,10 +1,11 @@
 """GPU parity over seeded random shapes: batch, length (ragged and exact multiples of 64), KV heads,
 group size, head dim, K (up to 32, beyond the number of leaves as well), input dtype and candidate
 score, drawn once from a fixed seed so the list is the same on every run.  Every token of every
-case goes through the oracle comparison of the parity tests (pyramid, selections under the boundary
-rule, leaf scores, attention end to end and on the oracle's own selection; the variant cases compare
-selections and leaf scores), and the boundary mismatches are pooled over all cases against the 0.1%
-budget.
+prefill case goes through the oracle comparison of the parity tests (pyramid, selections under the
+boundary rule, leaf scores, attention end to end and on the oracle's own selection; the variant
+cases compare selections and leaf scores); every step of every decode case is compared with the
+decode oracle (selection, output, and the incremental pyramid against a rebuild).  The boundary
+mismatches are pooled over all cases of a test against the 0.1% budget.
 """
 from __future__ import annotations
 
@@ -13,7 +14,7 @@ import pytest
 
 import gpu_harness as H
 from hierarchical_top_selection_amd import workloads as W
-from test_gpu_parity import check_prefill
+from test_gpu_parity import check_prefill, run_decode
 from test_gpu_variants import check_variant
 
 pytestmark = pytest.mark.gpu
@@ -50,3 +51,32 @@ def test_random_shapes_pooled_budget():
     n_bad = sum(c[0] for c in counts)
     n_total = sum(c[1] for c in counts)
     H.assert_mismatch_budget(n_bad, n_total, "random shapes")
+
+
+def decode_cases(count: int = 40):
+    rng = np.random.default_rng(2025)
+    out = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        k = int(rng.integers(1, min(16, 128 // g) + 1))          # G * 2K <= 256 (leaf logits on chip)
+        d = int(rng.choice([64, 128]))
+        n0 = int(rng.choice([int(rng.integers(1, 3000)), 64 * int(rng.integers(1, 40)) - 1]))
+        steps = int(rng.integers(5, 81))
+        b = int(rng.integers(1, 3))
+        dtype = "f32" if i % 5 == 4 else "bf16"
+        out.append((dict(n_kv_heads=hkv, n_q_heads=g * hkv, top_k=k, head_dim=d, decode_steps=steps, dtype=dtype,
+                         seed=400 + i), b, n0, steps))
+    return out
+
+
+def test_random_decode_shapes_pooled_budget():
+    counts = []
+    for i, (c, b, n0, steps) in enumerate(decode_cases()):
+        w = W.WORKLOADS["decode_b64_ctx131072"].with_(name=f"dec_rand{i}", **c)
+        label = (f"dec_rand{i}_b{b}_ctx{n0}_s{steps}_hkv{w.n_kv_heads}_g{w.group}_d{w.head_dim}_k{w.top_k}_"
+                 f"{w.dtype}")
+        run_decode(w, list(range(b)), n0, steps, label, counts=counts)
+    n_bad = sum(c[0] for c in counts)
+    n_total = sum(c[1] for c in counts)
+    H.assert_mismatch_budget(n_bad, n_total, "random decode shapes")
