@@ -4,16 +4,19 @@ score, drawn once from a fixed seed so the list is the same on every run.  Every
 prefill case goes through the oracle comparison of the parity tests (pyramid, selections under the
 boundary rule, leaf scores, attention end to end and on the oracle's own selection; the variant
 cases compare selections and leaf scores); every step of every decode case is compared with the
-decode oracle (selection, output, and the incremental pyramid against a rebuild).  The boundary
+decode oracle (selection, output, and the incremental pyramid against a rebuild); every gradient of
+every backward case is compared with the oracle's (the backward tests' tolerances).  The boundary
 mismatches are pooled over all cases of a test against the 0.1% budget.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
+import torch
 
 import gpu_harness as H
 from hierarchical_top_selection_amd import workloads as W
+from test_gpu_backward import check_full
 from test_gpu_parity import check_prefill, run_decode
 from test_gpu_variants import check_variant
 
@@ -80,3 +83,26 @@ def test_random_decode_shapes_pooled_budget():
     n_bad = sum(c[0] for c in counts)
     n_total = sum(c[1] for c in counts)
     H.assert_mismatch_budget(n_bad, n_total, "random decode shapes")
+
+
+def backward_cases(count: int = 16):
+    rng = np.random.default_rng(2026)
+    out = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.choice([int(rng.integers(1, 2000)), 64 * int(rng.integers(1, 30))]))
+        b = int(rng.integers(1, 3)) if n * hkv <= 1500 else 1
+        d = int(rng.choice([64, 128]))
+        k = int(rng.integers(1, 33))
+        out.append((dict(batch=b, seq_len=n, n_kv_heads=hkv, n_q_heads=g * hkv, head_dim=d, seed=500 + i), k,
+                    ("route", "random")[i % 2], (torch.float32, torch.bfloat16)[(i // 2) % 2]))
+    return out
+
+
+def test_random_backward_shapes():
+    for i, (c, k, selection, grad_dtype) in enumerate(backward_cases()):
+        w = W.WORKLOADS["prefill_n4096"].with_(name=f"bwd_rand{i}", **c)
+        label = (f"bwd_rand{i}_b{w.batch}_n{w.seq_len}_hkv{w.n_kv_heads}_g{w.group}_d{w.head_dim}_k{k}_{selection}_"
+                 f"{str(grad_dtype).split('.')[-1]}")
+        check_full(w, k, label, selection=selection, grad_dtype=grad_dtype)
