@@ -5,7 +5,8 @@ prefill case goes through the oracle comparison of the parity tests (pyramid, se
 boundary rule, leaf scores, attention end to end and on the oracle's own selection; the variant
 cases compare selections and leaf scores); every step of every decode case is compared with the
 decode oracle (selection, output, and the incremental pyramid against a rebuild); every gradient of
-every backward case is compared with the oracle's (the backward tests' tolerances).  The boundary
+every backward case is compared with the oracle's (the backward tests' tolerances); every token of
+every flat-selection case is compared with the oracle's single-level selection.  The boundary
 mismatches are pooled over all cases of a test against the 0.1% budget.
 """
 from __future__ import annotations
@@ -17,6 +18,7 @@ import torch
 import gpu_harness as H
 from hierarchical_top_selection_amd import workloads as W
 from test_gpu_backward import check_full
+from test_gpu_flat import check_flat
 from test_gpu_parity import check_prefill, run_decode
 from test_gpu_variants import check_variant
 
@@ -106,3 +108,27 @@ def test_random_backward_shapes():
         label = (f"bwd_rand{i}_b{w.batch}_n{w.seq_len}_hkv{w.n_kv_heads}_g{w.group}_d{w.head_dim}_k{k}_{selection}_"
                  f"{str(grad_dtype).split('.')[-1]}")
         check_full(w, k, label, selection=selection, grad_dtype=grad_dtype)
+
+
+def flat_cases(count: int = 16):
+    rng = np.random.default_rng(2027)
+    out = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.choice([int(rng.integers(1, 3000)), 64 * int(rng.integers(1, 45))]))
+        b = int(rng.integers(1, 3)) if n * hkv <= 2000 else 1
+        out.append((dict(batch=b, seq_len=n, n_kv_heads=hkv, n_q_heads=g * hkv, head_dim=int(rng.choice([64, 128])),
+                         dtype="f32" if i % 5 == 4 else "bf16", seed=600 + i), int(rng.integers(1, 17))))
+    return out
+
+
+def test_random_flat_shapes_pooled_budget():
+    counts = []
+    for i, (c, k) in enumerate(flat_cases()):
+        w = W.WORKLOADS["prefill_n4096"].with_(name=f"flat_rand{i}", **c)
+        label = f"flat_rand{i}_b{w.batch}_n{w.seq_len}_hkv{w.n_kv_heads}_g{w.group}_d{w.head_dim}_k{k}_{w.dtype}"
+        check_flat(w, k, label, counts=counts)
+    n_bad = sum(c[0] for c in counts)
+    n_total = sum(c[1] for c in counts)
+    H.assert_mismatch_budget(n_bad, n_total, "random flat shapes")
