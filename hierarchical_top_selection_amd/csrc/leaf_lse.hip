@@ -24,7 +24,7 @@ namespace pisa {
 // Blocks are mapped to windows XCD by XCD: workgroup L runs on XCD L % 8 (kXcds), and XCD x
 // walks windows x, x + 8, x + 16, ... so one window's query rows stay in one L2.
 
-constexpr int kItemsPerWave = 4;
+constexpr int kItemsPerWave = 2;
 // a wave's pairs fit two registers per lane, and its items the four-way picks below
 static_assert(kItemsPerWave <= 4 && kItemsPerWave * kPairsPerItem <= 128, "wave pair stream too long");
 
