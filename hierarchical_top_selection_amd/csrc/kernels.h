@@ -53,7 +53,7 @@ struct RouteArgs {
 
 // Stage-2 work is cut into items of at most kPairsPerItem (token, slot) pairs of one
 // leaf in one window, so a leaf that many queries share is spread over many waves.
-constexpr int kPairsPerItem = 32;
+constexpr int kPairsPerItem = 16;
 
 struct ClusterArgs {
   const int32_t* cand;   // [B*Hkv][N][2K]
