@@ -33,8 +33,9 @@ struct StageScope {
 constexpr int kMaxSeqSelect = 1000000;     // leaf counters of one window must fit in LDS
 constexpr int kMaxSeq = (1 << 25) - 1;     // packed (token << 6 | slot) fits int32
 // Tokens per Stage-2 clustering window: a window's query rows and the key blocks its
-// items stream share the L2; measured best at 512 tokens up to 64K and 1024 above.
-int window_tokens(int seq_len) { return seq_len <= 65536 ? 512 : 1024; }
+// items stream share the L2; measured best at 512 tokens up to 64K and 2048 above (with
+// items of at most 16 pairs; 1024 and 4096 are slower at 256K, 1024 at 32K).
+int window_tokens(int seq_len) { return seq_len <= 65536 ? 512 : 2048; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -116,7 +116,7 @@ __device__ inline void leaf_pair(const typename RawFrag<T, D>::type (&kf)[4], co
 // Each wave walks kItemsPerWave consecutive items of one window as one stream of pairs:
 // the query rows are fetched kAhead pairs ahead (across item boundaries), and consecutive
 // items of the same leaf keep their keys.  Two pairs ahead at three waves per SIMD suits the
-// 1024-token windows of long sequences, whose query rows often come from beyond the L2; one
+// longer windows of long sequences, whose query rows come from beyond the L2 more often; one
 // pair ahead at four waves per SIMD (128 VGPRs) the 512-token windows, whose rows mostly hit
 // it (measured: 2.46 -> 2.34 ms at 32K, 3.37 -> 3.49 ms at 256K).
 // fp32 keys at d = 128 need 128 VGPRs of fragments: no occupancy target there.
